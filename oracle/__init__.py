@@ -1,0 +1,109 @@
+"""CPU oracle for the fused multi-head attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench
+script's CPU-baseline leg may import this package. The HIP library and its
+Python binding never import it, and it imports nothing from them.
+
+`fmha_oracle.c` holds the arithmetic: the plain fp64 definition
+softmax(scale * Q K^T) V, plus the natural-log logsumexp of each row, one
+query row at a time. The pages name the stages: QK^T, then softmax, then PV
+(Tawa, section III-D), and the load/mma/softmax/rescale tasks (PipeThreader,
+"core method"). This module only builds the C library and marshals arrays
+for it.
+
+Every function here is pinned by `tests/test_oracle.py`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fmha_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile fmha_oracle.c with gcc into liboracle.so (next to the source)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                        _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_fmha_rows.restype = ctypes.c_int
+        lib.oracle_fmha_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_half_to_double.restype = None
+        lib.oracle_half_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int64]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def half_to_double(bits: np.ndarray) -> np.ndarray:
+    """Widen binary16 values (given as float16 or uint16 arrays) to float64."""
+    a = np.ascontiguousarray(bits).view(np.uint16)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().oracle_half_to_double(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def _as_half(x: np.ndarray) -> np.ndarray:
+    if x.dtype != np.float16:
+        raise TypeError("oracle inputs are float16 arrays, got %s" % x.dtype)
+    return np.ascontiguousarray(x)
+
+
+def fmha_rows(q, k, v, rows, *, causal: bool, scale, threads: int | None = None):
+    """Output rows and logsumexp for the given (b, h, i) triples.
+
+    q, k, v: float16 [B, H, N, d]. rows: int [n, 3].
+    Returns (o float64 [n, d], lse float64 [n]).
+    """
+    q, k, v = _as_half(q), _as_half(k), _as_half(v)
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    st = _load().oracle_fmha_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, N, d, int(bool(causal)),
+        float(scale), rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data,
+        int(threads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_fmha_rows failed with status %d" % st)
+    return o, lse
+
+
+def fmha_all(q, k, v, *, causal: bool, scale, threads: int | None = None):
+    """Every row: returns (o float64 [B,H,N,d], lse float64 [B,H,N])."""
+    B, H, N, d = q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+    o, lse = fmha_rows(q, k, v, rows, causal=causal, scale=scale, threads=threads)
+    return o.reshape(B, H, N, d), lse.reshape(B, H, N)

@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the HIP path's callers (tests, bench) and by the CPU
+oracle's callers. It draws numbers and picks rows. It holds no part of the
+attention arithmetic.
+
+Workloads. Each page evaluates FMHA forward in FP16 with batch 4, 32 heads and
+head dim 128, at sequence lengths from 1K to 16K:
+- Twill (OSDI'26), section 6.2 and Figures 7-8;
+- Tawa (CGO'26), section V-D and Figure 10.
+The pages measure no dataset. Inputs are i.i.d. N(0,1) draws rounded to fp16,
+in the [B, H, N, d] layout.
+
+Recipe, per workload index c:
+- rng = numpy.random.default_rng(20260000 + c);
+- draw Q, K, V in that order, each as float32 standard_normal of shape
+  [B, H, N, d], then round once to float16 (round-to-nearest-even);
+- the causal workload's K is fp16(3 * z), with the product taken in float32;
+- scale = float32(1 / sqrt(d)).
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED_BASE = 20260000
+SAMPLE_SEED_XOR = 0x5EED
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    k_gain: float = 1.0       # K = fp16(k_gain * z)
+    sampled_rows: int = 0     # 0: the oracle checks every row
+
+    @property
+    def flops(self) -> float:
+        """Counted work: 4*B*H*N^2*d. Causal counts half of it."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    @property
+    def scale(self) -> np.float32:
+        return np.float32(1.0 / np.sqrt(np.float64(self.d)))
+
+
+WORKLOADS = (
+    Workload("tiny_b1h1n128d64", 1, 1, 128, 64, False),
+    Workload("b4h32n1024d128", 4, 32, 1024, 128, False),
+    Workload("b4h32n4096d128", 4, 32, 4096, 128, False, sampled_rows=256),
+    Workload("b4h32n16384d128", 4, 32, 16384, 128, False, sampled_rows=256),
+    Workload("causal_b4h32n8192d128_k3", 4, 32, 8192, 128, True, k_gain=3.0,
+             sampled_rows=256),
+)
+HEADLINE = 3
+
+
+def draw_qkv(B: int, H: int, N: int, d: int, seed: int, k_gain: float = 1.0):
+    """Q, K, V as float16 arrays of shape [B,H,N,d], drawn in that order."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    out = []
+    for name in ("q", "k", "v"):
+        z = rng.standard_normal(size=shape, dtype=np.float32)
+        if name == "k" and k_gain != 1.0:
+            z *= np.float32(k_gain)
+        out.append(z.astype(np.float16))
+        del z
+    return tuple(out)
+
+
+def workload_inputs(index: int):
+    """(q, k, v, scale) for WORKLOADS[index]."""
+    w = WORKLOADS[index]
+    q, k, v = draw_qkv(w.B, w.H, w.N, w.d, SEED_BASE + index, w.k_gain)
+    return q, k, v, w.scale
+
+
+def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:
+    """n distinct (b, h, i) triples, uniform over B*H*N, sorted by flat index."""
+    rng = np.random.default_rng(seed)
+    total = B * H * N
+    n = min(n, total)
+    flat = np.sort(rng.choice(total, size=n, replace=False))
+    b, rem = np.divmod(flat, H * N)
+    h, i = np.divmod(rem, N)
+    return np.stack([b, h, i], axis=1).astype(np.int64)
+
+
+def boundary_rows(B: int, H: int, N: int, heads: int, seed: int,
+                  tiles=(64, 128)) -> np.ndarray:
+    """Rows at tile edges of a few seeded heads: 0, 1, t-1, t for each tile
+    size t, and N-1."""
+    rng = np.random.default_rng(seed)
+    picks = rng.choice(B * H, size=min(heads, B * H), replace=False)
+    idx = {0, 1, N - 1}
+    for t in tiles:
+        idx.update({t - 1, t})
+    idx = sorted(i for i in idx if 0 <= i < N)
+    rows = [(p // H, p % H, i) for p in sorted(picks) for i in idx]
+    return np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+
+
+def workload_rows(index: int) -> np.ndarray:
+    """The (b,h,i) triples the oracle checks for WORKLOADS[index]."""
+    w = WORKLOADS[index]
+    seed = (SEED_BASE + index) ^ SAMPLE_SEED_XOR
+    if w.sampled_rows == 0:
+        b, h, i = np.meshgrid(np.arange(w.B), np.arange(w.H), np.arange(w.N),
+                              indexing="ij")
+        return np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int64)
+    rows = sample_rows(w.B, w.H, w.N, w.sampled_rows, seed)
+    if w.causal:
+        extra = boundary_rows(w.B, w.H, w.N, 4, seed + 1)
+        rows = np.unique(np.concatenate([rows, extra]), axis=0)
+    return rows
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
