@@ -1,0 +1,86 @@
+/*
+ * fmha.h - C ABI of the MI355X (gfx950) fused multi-head attention forward
+ * pass.
+ *
+ * The operation. For every batch b, head h and query row i:
+ *   S   = scale * Q K^T      (one row: s_j = scale * q_i . k_j)
+ *   P   = softmax(S)         (over the keys j visible to row i)
+ *   O   = P V
+ *   lse = log(sum_j exp(s_j))   (natural log of the scaled scores)
+ * The pages split this into three stages. Tawa (CGO'26), section III-D,
+ * coarse-grained pipeline: QK^T is the tensor-core stage T, softmax is the
+ * stage C, and PV is the stage U. PipeThreader (OSDI'25) lists load, mma,
+ * softmax and rescale tasks. Twill (OSDI'26), section 6.2, and Tawa,
+ * section V-D, evaluate the FP16 forward kernel with batch 4, 32 heads and
+ * head dim 128.
+ *
+ * The library computes it in one fused kernel. Each step of the path runs
+ * in the library's own HIP kernels. It allocates no device memory and keeps
+ * no per-call state.
+ */
+#ifndef FMHA_H
+#define FMHA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by fmha_fwd. */
+#define FMHA_OK 0
+#define FMHA_ERR_INVALID_ARGUMENT 1 /* null pointer, negative size, non-finite scale, aliasing outputs */
+#define FMHA_ERR_UNSUPPORTED 2      /* head dim, scale sign, alignment or size outside what the kernel handles */
+#define FMHA_ERR_HIP 3              /* the kernel launch itself failed */
+
+/*
+ * fmha_fwd - enqueue the attention forward pass on `stream`.
+ *
+ * q, k, v : device pointers to IEEE binary16 tensors, contiguous [B, H, N, d]
+ *           (row i of head (b, h) starts at ((b*H + h)*N + i)*d elements).
+ *           Queries and keys have the same length N (self-attention).
+ * o       : device pointer, binary16 [B, H, N, d], written.
+ * lse     : device pointer, float32 [B, H, N], written. It holds the natural-log
+ *           logsumexp of row i's scaled scores over its visible keys.
+ * B, H, N : batch, heads, sequence length. Each must be >= 0. If any is 0 the
+ *           call returns FMHA_OK and enqueues nothing; the pointers are then
+ *           not examined (empty tensors may have null data pointers).
+ * d       : head dimension, 64 or 128.
+ * causal  : non-zero means key j is visible to query i only if j <= i (square,
+ *           top-left aligned). Zero means every key is visible.
+ * scale   : multiplier on q.k before the softmax; finite and > 0 (the usual
+ *           value is 1/sqrt(d)).
+ * stream  : hipStream_t to enqueue on (NULL = the default stream).
+ *
+ * Ownership. All five buffers are caller-owned device memory on the current
+ * device. Inputs are only read. o and lse must not overlap q, k, v or each
+ * other. The call is asynchronous: it returns once the kernel is enqueued, and
+ * outputs are valid after the stream is synchronised. It is thread-safe.
+ *
+ * Errors. On FMHA_ERR_INVALID_ARGUMENT or FMHA_ERR_UNSUPPORTED nothing is
+ * enqueued and no HIP call is made. FMHA_ERR_HIP reports a failed launch.
+ * Faults inside the kernel surface at the caller's next synchronisation.
+ * Nothing is printed; no C++ exception crosses this boundary.
+ *
+ * Limits (else FMHA_ERR_UNSUPPORTED):
+ * - q, k, v and o aligned to 16 bytes, lse to 4;
+ * - (N + 256) * d * 2 < 2^31 bytes per head;
+ * - the grid B*H*ceil(N/tile) < 2^31.
+ */
+int fmha_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* fmha_status_str - static, human-readable text for a status code. */
+const char *fmha_status_str(int status);
+
+/* fmha_query_tile - query rows per workgroup of the kernel fmha_fwd launches
+ * for head dim d (0 if d is unsupported). Bench and tests use it to size grids
+ * and pick tile-edge rows. */
+int fmha_query_tile(int d);
+
+/* fmha_key_tile - keys per pipeline stage of that kernel (0 if unsupported). */
+int fmha_key_tile(int d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMHA_H */

@@ -1,0 +1,96 @@
+// C ABI of the attention forward pass: argument checks, variant choice, and
+// the launch on the caller's stream. The operation and the error contract
+// are stated in include/fmha.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fmha.h"
+#include "fmha_fwd_kernel.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+template <int D, bool CAUSAL>
+int launch(const fmha::Params& prm, hipStream_t stream) {
+  using T = fmha::Tile<D>;
+  void* args[] = {const_cast<fmha::Params*>(&prm)};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_fwd_kernel<D, CAUSAL>),
+                                       dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+template <int D>
+int tile_rows() { return fmha::Tile<D>::BM; }
+
+}  // namespace
+
+extern "C" int fmha_query_tile(int d) {
+  if (d == 64) return fmha::Tile<64>::BM;
+  if (d == 128) return fmha::Tile<128>::BM;
+  return 0;
+}
+
+extern "C" int fmha_key_tile(int d) {
+  if (d == 64) return fmha::Tile<64>::BN;
+  if (d == 128) return fmha::Tile<128>::BN;
+  return 0;
+}
+
+extern "C" int fmha_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int N, int d, int causal, float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || N == 0) return FMHA_OK;  // empty: nothing to do, pointers unused
+  if (!q || !k || !v || !o || !lse) return FMHA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f)) return FMHA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FMHA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FMHA_ERR_UNSUPPORTED;
+  // byte offsets inside one head are 32-bit, with room for a ragged tile
+  if ((static_cast<int64_t>(N) + 256) * d * 2 >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+
+  const int bm = fmha_query_tile(d);
+  const int64_t n_qt = (N + bm - 1) / bm;
+  const int64_t grid = static_cast<int64_t>(B) * H * n_qt;
+  if (grid >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+
+  const uint64_t tbytes = static_cast<uint64_t>(B) * H * N * d * 2;
+  const uint64_t lbytes = static_cast<uint64_t>(B) * H * N * 4;
+  if (overlap(o, tbytes, q, tbytes) || overlap(o, tbytes, k, tbytes) || overlap(o, tbytes, v, tbytes) ||
+      overlap(lse, lbytes, q, tbytes) || overlap(lse, lbytes, k, tbytes) ||
+      overlap(lse, lbytes, v, tbytes) || overlap(lse, lbytes, o, tbytes))
+    return FMHA_ERR_INVALID_ARGUMENT;
+
+  fmha::Params prm;
+  prm.q = static_cast<const _Float16*>(q);
+  prm.k = static_cast<const _Float16*>(k);
+  prm.v = static_cast<const _Float16*>(v);
+  prm.o = static_cast<_Float16*>(o);
+  prm.lse = lse;
+  prm.N = N;
+  prm.n_qt = static_cast<int>(n_qt);
+  prm.total_wg = static_cast<int>(grid);
+  prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 64) return causal ? launch<64, true>(prm, s) : launch<64, false>(prm, s);
+  return causal ? launch<128, true>(prm, s) : launch<128, false>(prm, s);
+}
+
+extern "C" const char* fmha_status_str(int status) {
+  switch (status) {
+    case FMHA_OK: return "ok";
+    case FMHA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported shape, alignment or scale";
+    case FMHA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}

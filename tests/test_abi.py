@@ -1,0 +1,113 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/fmha.h declares, and rejects bad arguments before any HIP call (so
+no GPU is needed here)."""
+import math
+import os
+import re
+
+import pytest
+
+from software_pipelining_fmha_amd import fmha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmha.h")
+
+A = 1 << 20  # a fake, 16-byte aligned "device address" (never dereferenced)
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fmha_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(fmha.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fmha.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, N=128, d=128, causal=0,
+         scale=0.125):
+    return fmha.fmha_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointer_is_invalid(which):
+    assert call(**{which: 0}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field", ["B", "H", "N"])
+def test_negative_size_is_invalid(field):
+    assert call(**{field: -1}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_non_finite_scale_is_invalid(scale):
+    assert call(scale=scale) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_non_positive_scale_is_unsupported(scale):
+    assert call(scale=scale) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 256, -64])
+def test_head_dim_outside_64_128_is_unsupported(d):
+    assert call(d=d) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which,off", [("q", 8), ("k", 2), ("v", 4), ("o", 8), ("lse", 2)])
+def test_misaligned_pointer_is_unsupported(which, off):
+    base = {"q": A, "k": 2 * A, "v": 3 * A, "o": 4 * A, "lse": 5 * A}[which]
+    assert call(**{which: base + off}) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+def test_head_too_long_is_unsupported():
+    # (N + 256) * d * 2 bytes per head must stay below 2^31
+    assert call(N=(1 << 23), d=128) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+def test_grid_too_large_is_unsupported():
+    assert call(B=1 << 20, H=1 << 10, N=1 << 14, q=1 << 50, k=2 << 50, v=3 << 50, o=4 << 50,
+                lse=5 << 50) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_output_aliasing_input_is_invalid(which):
+    kw = {which: 4 * A}  # same address as o
+    assert call(**kw) == fmha.FMHA_ERR_INVALID_ARGUMENT
+    kw = {which: 5 * A}  # same address as lse
+    assert call(**kw) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+def test_lse_overlapping_o_is_invalid():
+    assert call(lse=4 * A + 64) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field", ["B", "H", "N"])
+def test_empty_problem_is_ok_and_launches_nothing(field):
+    # returns before any HIP call, so it runs without a GPU
+    assert call(**{field: 0}) == fmha.FMHA_OK
+
+
+def test_status_strings():
+    for s in range(4):
+        assert fmha.fmha_status_str(s) and fmha.fmha_status_str(s) != "unknown status"
+    assert fmha.fmha_status_str(99) == "unknown status"
+
+
+def test_tiles_reported():
+    for d in (64, 128):
+        assert fmha.fmha_query_tile(d) > 0 and fmha.fmha_key_tile(d) > 0
+    assert fmha.fmha_query_tile(96) == 0 and fmha.fmha_key_tile(96) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(fmha, "_lib", None)
+    monkeypatch.setattr(fmha, "_LIB_PATH", "/nonexistent/libfmha.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        fmha.lib()

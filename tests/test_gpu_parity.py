@@ -1,0 +1,207 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: max |O - O_oracle| <= 2e-3 and max |lse - lse_oracle| <= 1e-3, for
+fp16 inputs, on every checked row.
+
+Workloads: FP16, batch 4, 32 heads, head dim 128, sequence lengths 1K-16K.
+Twill, section 6.2, and Tawa, section V-D, evaluate this shape. Inputs are
+seeded i.i.d. N(0,1) draws. Small shapes are compared on every row. At full
+size the test compares the sampled rows the oracle computes one by one. A
+uniform-key property holds at any size and checks every row's O and lse in
+closed form.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from software_pipelining_fmha_amd import fmha, inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-3
+TOL_LSE = 1e-3
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev(*arrays):
+    torch = torch_mod()
+    return [torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0") for a in arrays]
+
+
+def run(q, k, v, causal, scale, fill_nan=True, stream=None):
+    """fmha_fwd on the GPU. Outputs start as NaN so unwritten rows show."""
+    torch = torch_mod()
+    tq, tk, tv = to_dev(q, k, v)
+    B, H, N, d = q.shape
+    o = torch.full((B, H, N, d), float("nan") if fill_nan else 0.0, dtype=torch.float16,
+                   device="cuda:0")
+    lse = torch.full((B, H, N), float("nan") if fill_nan else 0.0, dtype=torch.float32,
+                     device="cuda:0")
+    fmha.forward(tq, tk, tv, causal=causal, scale=float(scale), out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref, label):
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    og = o_gpu[b, h, i].astype(np.float64)
+    lg = lse_gpu[b, h, i].astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), label + ": non-finite output"
+    eo = np.abs(og - o_ref).max()
+    el = np.abs(lg - lse_ref).max()
+    print("%s: rows=%d max|dO|=%.3e max|dlse|=%.3e" % (label, len(rows), eo, el), flush=True)
+    assert eo <= TOL_O, "%s: O error %.3e" % (label, eo)
+    assert el <= TOL_LSE, "%s: lse error %.3e" % (label, el)
+
+
+@pytest.mark.parametrize("idx", range(len(inputs.WORKLOADS)),
+                         ids=[w.name for w in inputs.WORKLOADS])
+def test_workload_parity(idx, device):
+    w = inputs.WORKLOADS[idx]
+    print("workload %s" % w.name, flush=True)
+    q, k, v, scale = inputs.workload_inputs(idx)
+    o, lse = run(q, k, v, w.causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten or NaN output"
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = inputs.workload_rows(idx)
+    o_ref, lse_ref = oracle.fmha_rows(q, k, v, rows, causal=w.causal, scale=scale)
+    check_rows(o, lse, rows, o_ref, lse_ref, w.name)
+
+
+RAGGED = [(2, 3, n, d, c) for n in (1, 2, 63, 65, 127, 129, 200, 333) for d in (64, 128)
+          for c in (False, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", RAGGED)
+def test_ragged_and_small_shapes(B, H, N, d, causal, device):
+    print("ragged B=%d H=%d N=%d d=%d causal=%d" % (B, H, N, d, causal), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=1000 + N * 7 + d + causal)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    check_rows(o, lse, rows, o_ref.reshape(-1, d), lse_ref.reshape(-1), "ragged")
+
+
+@pytest.mark.parametrize("N,causal", [(16384, False), (8192, True)])
+def test_full_size_uniform_keys_every_row(N, causal, device):
+    """With every key row equal, O_i is the mean of the visible value rows and
+    lse_i = scale*q_i.u + ln|J_i|. Every (b, h, i) row of the full-size
+    workload is checked. Outputs start as NaN, so a tile the grid misses
+    would fail."""
+    B, H, d = 4, 32, 128
+    print("uniform-K full size N=%d causal=%d" % (N, causal), flush=True)
+    q, _, v = inputs.draw_qkv(B, H, N, d, seed=777 + N)
+    u = np.random.default_rng(5).standard_normal((B, H, 1, d)).astype(np.float16)
+    k = np.ascontiguousarray(np.broadcast_to(u, (B, H, N, d)))
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    s = float(scale) * np.einsum("bhnd,bhd->bhn", q.astype(np.float64), u[:, :, 0].astype(np.float64))
+    if causal:
+        cnt = np.arange(1, N + 1, dtype=np.float64)
+        mean = np.cumsum(v.astype(np.float64), axis=2) / cnt[None, None, :, None]
+        lse_ref = s + np.log(cnt)[None, None, :]
+    else:
+        mean = np.broadcast_to(v.astype(np.float64).mean(axis=2, keepdims=True), v.shape)
+        lse_ref = s + math.log(N)
+    eo = np.abs(o.astype(np.float64) - mean).max()
+    el = np.abs(lse.astype(np.float64) - lse_ref).max()
+    print("uniform-K: max|dO|=%.3e max|dlse|=%.3e" % (eo, el), flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_hot_scores_select_one_value_row(d, device):
+    N = 300
+    q = np.zeros((1, 2, N, d), np.float16)
+    k = np.zeros((1, 2, N, d), np.float16)
+    v = inputs.draw_qkv(1, 2, N, d, seed=9)[2]
+    jstar = 217
+    q[..., 5] = 64
+    k[:, :, jstar, 5] = 64
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, False, scale)
+    assert np.array_equal(o, np.broadcast_to(v[:, :, jstar:jstar + 1], o.shape))
+    assert np.abs(lse - 4096 * float(scale)).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_first_row_is_first_value_row(d, device):
+    q, k, v = inputs.draw_qkv(2, 2, 257, d, seed=12)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, True, scale)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    s0 = float(scale) * np.einsum("bhd,bhd->bh", q[:, :, 0].astype(np.float64),
+                                  k[:, :, 0].astype(np.float64))
+    assert np.abs(lse[:, :, 0] - s0).max() <= TOL_LSE
+
+
+def test_key_permutation_invariance(device):
+    q, k, v = inputs.draw_qkv(1, 4, 1000, 128, seed=13)
+    scale = np.float32(1 / math.sqrt(128))
+    o, lse = run(q, k, v, False, scale)
+    perm = np.random.default_rng(3).permutation(1000)
+    o2, lse2 = run(q, k[:, :, perm], v[:, :, perm], False, scale)
+    assert np.abs(o.astype(np.float64) - o2).max() <= TOL_O
+    assert np.abs(lse.astype(np.float64) - lse2).max() <= TOL_LSE
+
+
+def test_deterministic_bitwise(device):
+    q, k, v, scale = inputs.workload_inputs(1)
+    a = run(q, k, v, False, scale)
+    b = run(q, k, v, False, scale)
+    assert np.array_equal(a[0].view(np.uint16), b[0].view(np.uint16))
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_non_default_stream(device):
+    torch = torch_mod()
+    q, k, v = inputs.draw_qkv(2, 2, 500, 128, seed=14)
+    scale = np.float32(1 / math.sqrt(128))
+    ref = run(q, k, v, True, scale)
+    s = torch.cuda.Stream()
+    got = run(q, k, v, True, scale, stream=s)
+    assert np.array_equal(ref[0].view(np.uint16), got[0].view(np.uint16))
+
+
+def test_guard_bands_untouched(device):
+    """Writes stay inside o and lse: sentinels around both are unchanged."""
+    torch = torch_mod()
+    B, H, N, d = 2, 2, 333, 128
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=15)
+    tq, tk, tv = to_dev(q, k, v)
+    pad = 4096
+    ob = torch.full((B * H * N * d + 2 * pad,), 12345.0, dtype=torch.float16, device="cuda:0")
+    lb = torch.full((B * H * N + 2 * pad,), -777.0, dtype=torch.float32, device="cuda:0")
+    o = ob[pad:pad + B * H * N * d].view(B, H, N, d)
+    lse = lb[pad:pad + B * H * N].view(B, H, N)
+    fmha.forward(tq, tk, tv, causal=True, scale=0.088388, out=o, lse=lse)
+    torch.cuda.synchronize()
+    obc, lbc = ob.cpu().numpy(), lb.cpu().numpy()
+    assert (obc[:pad] == np.float16(12345.0)).all() and (obc[-pad:] == np.float16(12345.0)).all()
+    assert (lbc[:pad] == -777.0).all() and (lbc[-pad:] == -777.0).all()
+    assert np.isfinite(obc[pad:-pad]).all()
+
+
+def test_other_scale_values(device):
+    q, k, v = inputs.draw_qkv(1, 3, 190, 64, seed=16)
+    for scale in (np.float32(0.02), np.float32(0.5)):
+        o, lse = run(q, k, v, True, scale)
+        o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=True, scale=scale)
+        rows = np.argwhere(np.ones((1, 3, 190), bool))
+        check_rows(o, lse, rows, o_ref.reshape(-1, 64), lse_ref.reshape(-1), "scale")
+
+
+def test_empty_problem_launches_nothing(device):
+    torch = torch_mod()
+    q = torch.empty((0, 2, 16, 64), dtype=torch.float16, device="cuda:0")
+    o, lse = fmha.forward(q, q.clone(), q.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and lse.numel() == 0
