@@ -1,0 +1,216 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fmha_fwd launch over the whole batch. The default workload is
+FP16, B=4, H=32, N=16384, d=128, non-causal; the Twill (section 6.2, Fig. 7)
+and Tawa (section V-D) evaluations use this shape at their longest sequence.
+Inputs are seeded synthetic N(0,1) draws and are already resident in HBM
+when the timed region starts. Throughput counts 4*B*H*N^2*d FLOPs per step,
+halved for causal.
+
+Prints one JSON line. It includes the MFMA roofline of the kernel (average
+launch time from HIP events on the launch stream) and, on rank 0, the CPU
+oracle timed on a bounded row sample. The oracle's rows also check the
+timed output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from software_pipelining_fmha_amd import inputs  # noqa: E402
+
+METRIC = "FMHA fwd TFLOPS (fp16, B4 H32 d128, N=16384) and % of MFMA peak"
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+KERNEL_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_kernel.hpp",
+                  "software_pipelining_fmha_amd/csrc/fmha_api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fmha_fwd_b4h32n16384d128.txt")
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source and this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_digest") != kernel_digest() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(q, k, v, w, scale, o_gpu, lse_gpu, target_s: float):
+    """Time the CPU oracle on a seeded row sample of the same workload, and
+    compare those rows with the GPU output."""
+    import oracle
+
+    threads = cpu_threads()
+    idx = inputs.WORKLOADS.index(w)
+    rows0 = inputs.workload_rows(idx) if w.sampled_rows else inputs.sample_rows(
+        w.B, w.H, w.N, 256, (inputs.SEED_BASE + idx) ^ inputs.SAMPLE_SEED_XOR)
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.fmha_rows(q, k, v, rows0, causal=w.causal, scale=scale, threads=threads)
+    t_first = time.perf_counter() - t0
+    b, h, i = rows0.T
+    err_o = float(np.abs(o_gpu[b, h, i].astype(np.float64) - o_ref).max())
+    err_l = float(np.abs(lse_gpu[b, h, i].astype(np.float64) - l_ref).max())
+
+    # grow the sample to about target_s seconds of oracle work
+    n = int(min(w.B * w.H * w.N, max(len(rows0), len(rows0) * target_s / max(t_first, 1e-3))))
+    rows = inputs.sample_rows(w.B, w.H, w.N, n, 4242 + idx)
+    t0 = time.perf_counter()
+    oracle.fmha_rows(q, k, v, rows, causal=w.causal, scale=scale, threads=threads)
+    dt = time.perf_counter() - t0
+    vis = (rows[:, 2] + 1).astype(np.float64) if w.causal else np.full(len(rows), float(w.N))
+    flops = float((4.0 * w.d * vis).sum())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "sample": "%d seeded (b,h,i) rows of %s, every visible key per row; %.1f s wall"
+                  % (len(rows), w.name, dt),
+        "seconds": dt,
+    }, {"rows": int(len(rows0)), "max_abs_o": err_o, "max_abs_lse": err_l,
+        "pass": bool(err_o <= 2e-3 and err_l <= 1e-3)}
+
+
+def copy_calibration(mib: int, steps: int) -> int:
+    """A plain copy kernel of known size: `steps` launches that each read and
+    write mib MiB."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(max(1, steps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
+                      "launches": max(1, steps)}), flush=True)
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=inputs.WORKLOADS[inputs.HEADLINE].name,
+                    choices=[w.name for w in inputs.WORKLOADS])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, run a plain device copy of this many MiB "
+                         "per step (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the attention forward pass here is a "
+              "single-GPU kernel with no cross-GPU path (asked for --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_mib:
+        return copy_calibration(args.copy_mib, args.steps)
+
+    from software_pipelining_fmha_amd import fmha
+
+    fmha.lib()  # fail loudly before any work if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = next(x for x in inputs.WORKLOADS if x.name == args.workload)
+    idx = inputs.WORKLOADS.index(w)
+    q, k, v, scale = inputs.workload_inputs(idx)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fmha.forward(tq, tk, tv, causal=w.causal, scale=float(scale), out=o, lse=lse,
+                     stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC if idx == inputs.HEADLINE else
+        "FMHA fwd TFLOPS (fp16, %s) and %% of MFMA peak" % w.name, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "k_gain": w.k_gain, "layout": "BHNd",
+                   "flops_per_step": w.flops, "seed": inputs.SEED_BASE + idx},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": recorded_traffic(w.name),
+                     "kernel_ms_avg": round(avg_ms, 4), "kernel_ms_min": round(min(launch_ms), 4),
+                     "kernel_digest": kernel_digest()},
+    }
+    if not args.no_cpu_baseline:
+        o_host, lse_host = o.cpu().numpy(), lse.cpu().numpy()
+        cb, parity = cpu_baseline(q, k, v, w, scale, o_host, lse_host, args.cpu_seconds)
+        cb.pop("seconds")
+        result["cpu_baseline"] = cb
+        result["parity"] = parity
+    print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        return 1
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -8,7 +8,7 @@
 //   rescale tasks): VALU, exp2 on the transcendental unit;
 // - U stage, O += P V: fp16 MFMA.
 //
-// Data layout choices (all in registers of one 64-lane wave):
+// Register layouts (one 64-lane wave):
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_f16. A lane of the accumulator then holds 16 keys of
 //   one query column. So the row max and row sum are in-lane reductions
@@ -27,12 +27,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fmha {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+
+// Reference-max slack (base 2) before O and l are rescaled.
+constexpr float RESCALE_LOG2 = 8.0f;
+
 
 struct Params {
   const _Float16* q;
@@ -48,29 +56,24 @@ struct Params {
 
 template <int D>
 struct Tile {
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;               // two groups of 4, one wave of each per SIMD
   static constexpr int THREADS = WAVES * 64;
   static constexpr int QW = 32;                 // query rows per wave
   static constexpr int BM = WAVES * QW;         // query rows per workgroup
   static constexpr int BN = 64;                 // keys per pipeline stage
+  static constexpr int KB = BN / 32;            // 32-key MFMA blocks per stage
   static constexpr int KSTEPS = D / 16;         // MFMA k-steps of QK^T
   static constexpr int DBLK = D / 32;           // 32-row blocks of O^T
   static constexpr int PSTEPS = BN / 16;        // MFMA k-steps of PV
-  // LDS rows padded by 16 bytes. With it, 8 (or 16) consecutive lanes
-  // reading 16 B at the same column of consecutive rows hit distinct banks.
-  static constexpr int K_STRIDE = D + 8;        // halfs per key row
-  static constexpr int VT_STRIDE = BN + 8;      // halfs per d row of V^T
-  static constexpr int K_TILE = BN * K_STRIDE;  // halfs
-  static constexpr int V_TILE = D * VT_STRIDE;  // halfs
-  static constexpr int STAGE = K_TILE + V_TILE; // halfs per ring slot
-  // K tile loader: 16-byte chunks, CPR per key row.
-  static constexpr int CPR = D / 8;
-  static constexpr int K_ROWS_PER_PASS = THREADS / CPR;
-  static constexpr int K_PASSES = BN / K_ROWS_PER_PASS;
-  // V tile loader: each unit is 4 keys x 8 d, transposed on the way to LDS.
-  static constexpr int V_UNITS = (BN / 4) * (D / 8);
-  static_assert(V_UNITS <= THREADS, "one V unit per thread at most");
-  static_assert(BN % K_ROWS_PER_PASS == 0, "K loader covers the tile");
+  static constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
+  static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
+  static constexpr int SLOTS = 3;               // ring depth for K and for V
+  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
+  // one tile = TILE_BYTES / 1024 wave-wide 16-byte-per-lane LDS-DMA loads
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;  // per tile
+  static_assert(LOADS_PER_TILE % WAVES == 0 && LOADS_PER_WAVE >= 1, "tile loads split over waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -84,9 +87,16 @@ __device__ __forceinline__ intx4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
-// Value of x in the partner lane (lane ^ 32) via v_permlane32_swap. After the
-// swap the two results hold {x[l], x[l^32]} in some order, so callers combine
-// them with a symmetric operation.
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (buffer_load_dwordx4 ... lds). lds_base must be uniform.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, int byte_off,
+                                              __attribute__((address_space(3))) void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, byte_off, 0, 0, 0);
+}
+
+// Value of x combined with the partner lane (lane ^ 32) via v_permlane32_swap.
+// After the swap the two results hold {x[l], x[l^32]} in some order, so they
+// are combined with a symmetric operation.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -96,20 +106,46 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Row of a key inside the LDS K tile: swap bits 2 and 3 (an involution).
-__device__ __forceinline__ int key_slot(int key) {
-  const int flip = ((key >> 2) ^ (key >> 3)) & 1;
-  return key ^ (flip * 0xC);
+// Key held by row p of an LDS K tile: bits 2 and 3 of p swapped (an involution).
+__device__ __forceinline__ int key_of_row(int p) {
+  const int flip = ((p >> 2) ^ (p >> 3)) & 1;
+  return p ^ (flip * 0xC);
+}
+
+// LDS byte offset of 16-byte chunk c of row p in a K tile. The chunk index is
+// XOR-swizzled with the row, so 16 lanes reading one chunk column of 16
+// consecutive rows hit 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_chunk_off(int p, int c) {
+  constexpr int CPR = D / 8;
+  return (p * CPR + (c ^ (p % CPR))) * 16;
+}
+
+// LDS byte offset of 16-byte chunk c of key row `key` in a V tile (row-major,
+// d contiguous). The swizzle 4*(key%4) makes the transposed 8-byte reads of
+// 4 consecutive keys x 4 chunks (one ds_read_b64_tr_b16 half-wave) hit 16
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_chunk_off(int key, int c) {
+  constexpr int CPR = D / 8;
+  return (key * CPR + (c ^ ((4 * (key & 3)) % CPR))) * 16;
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fmha_fwd_kernel(Params p) {
+__global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * T::STAGE];
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) half8 lds_half8;
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  // LDS: a 3-slot ring of K tiles and a 3-slot ring of V tiles.
+  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
+  lds_char* const k_ring = (lds_char*)smem_raw;
+  lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;  // waves w and w + 4 share a SIMD
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -136,7 +172,8 @@ __global__ __launch_bounds__(256, 2) void fmha_fwd_kernel(Params p) {
 
   // ---- Q tile -> VGPRs: B operand of S^T = K Q^T ---------------------------
   // lane column = query (l32), lane half hh holds d = 16*s + 8*hh .. +7.
-  const int qrow = q0 + wave * T::QW + l32;
+  const int wave_q_lo = q0 + wave * T::QW;
+  const int qrow = wave_q_lo + l32;
   half8 qf[T::KSTEPS];
 #pragma unroll
   for (int s = 0; s < T::KSTEPS; ++s)
@@ -147,131 +184,244 @@ __global__ __launch_bounds__(256, 2) void fmha_fwd_kernel(Params p) {
   for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled scores (base-2 domain)
+  float m_run = -INFINITY;  // reference max of scaled scores (base-2 domain)
   float l_run = 0.f;        // this lane's share of the running sum
 
   const int n_kv_all = (N + T::BN - 1) / T::BN;
   const int n_kv = CAUSAL ? min(n_kv_all, (q0 + T::BM + T::BN - 1) / T::BN) : n_kv_all;
+  // Tiles this wave computes: causal rows see no key past wave_q_lo + 31.
+  const int n_wave = CAUSAL ? min(n_kv, (wave_q_lo + T::QW - 1) / T::BN + 1) : n_kv;
 
-  // ---- K/V producer: HBM -> VGPRs -> LDS ring slot ---------------------------
-  const int k_chunk = tid % T::CPR;
-  const int k_row0 = tid / T::CPR;
-  const int v_kg = tid % (T::BN / 4);  // keys 4*v_kg .. +3
-  const int v_dg = tid / (T::BN / 4);  // d    8*v_dg .. +7
-  const bool v_active = tid < T::V_UNITS;
-  intx4 kreg[T::K_PASSES];
-  intx4 vreg[4];
-
-  auto fetch = [&](int j) {
-    const int j0 = j * T::BN;
+  // ---- producer: HBM -> LDS ring slot, no VGPR staging -----------------------
+  // Wave w issues LDS-DMA loads w*LOADS_PER_WAVE .. +LOADS_PER_WAVE-1 of a
+  // tile; load i fills the tile's LDS chunks 64*i .. 64*i+63 (one per lane),
+  // and each lane fetches the global chunk that the swizzled layout puts there.
+  int k_src[T::LOADS_PER_WAVE], v_src[T::LOADS_PER_WAVE];
 #pragma unroll
-    for (int r = 0; r < T::K_PASSES; ++r)
-      kreg[r] = load16(rk, ((j0 + k_row0 + r * T::K_ROWS_PER_PASS) * D + 8 * k_chunk) * 2);
-    if (v_active) {
+  for (int r = 0; r < T::LOADS_PER_WAVE; ++r) {
+    const int x = 64 * (wave * T::LOADS_PER_WAVE + r) + lane;  // LDS chunk index
+    const int row = x / T::CPR, slot = x % T::CPR;
+    const int kc = slot ^ (row % T::CPR);
+    k_src[r] = (key_of_row(row) * D + 8 * kc) * 2;
+    const int vc = slot ^ ((4 * (row & 3)) % T::CPR);
+    v_src[r] = (row * D + 8 * vc) * 2;
+  }
+  auto fetch = [&](const __amdgpu_buffer_rsrc_t& r, lds_char* ring, const int (&src)[T::LOADS_PER_WAVE],
+                   int j) __attribute__((always_inline)) {
+    lds_char* dst = ring + (j % T::SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = load16(rv, ((j0 + 4 * v_kg + r) * D + 8 * v_dg) * 2);
-    }
-  };
-  auto stage = [&](int slot) {
-    _Float16* ks = smem + slot * T::STAGE;
-    _Float16* vt = ks + T::K_TILE;
-#pragma unroll
-    for (int r = 0; r < T::K_PASSES; ++r) {
-      const int key = k_row0 + r * T::K_ROWS_PER_PASS;
-      *reinterpret_cast<intx4*>(ks + key_slot(key) * T::K_STRIDE + 8 * k_chunk) = kreg[r];
-    }
-    if (v_active) {
-      const half8 r0 = __builtin_bit_cast(half8, vreg[0]);
-      const half8 r1 = __builtin_bit_cast(half8, vreg[1]);
-      const half8 r2 = __builtin_bit_cast(half8, vreg[2]);
-      const half8 r3 = __builtin_bit_cast(half8, vreg[3]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        half4 w = {r0[c], r1[c], r2[c], r3[c]};
-        *reinterpret_cast<half4*>(vt + (8 * v_dg + c) * T::VT_STRIDE + 4 * v_kg) = w;
-      }
-    }
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
+      load16_to_lds(r, j * T::BN * D * 2 + src[i], dst + i * 1024);
   };
 
-  fetch(0);
-  stage(0);
-  if (n_kv > 1) fetch(1);
-  __syncthreads();
-
-  const float c2 = p.scale_log2;
-  const int wave_q_lo = q0 + wave * T::QW;
-
-  for (int j = 0; j < n_kv; ++j) {
-    const _Float16* ks = smem + (j & 1) * T::STAGE;
-    const _Float16* vt = ks + T::K_TILE;
-    const int j0 = j * T::BN;
-
-    // T stage: S^T = K Q^T for two 32-key blocks
-    floatx16 sacc[2];
+  // ---- consumer-side LDS offsets (per lane, constant over the loop) ----------
+  // QK^T A operand: row 32*kb + l32 of the K tile, chunk 2*s + hh. The
+  // swizzle depends on the row only through row % CPR, so the 32-row block kb
+  // adds a constant.
+  int k_rd[T::KSTEPS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int s = 0; s < T::KSTEPS; ++s) k_rd[s] = k_chunk_off<D>(l32, 2 * s + hh);
+  constexpr int K_BLOCK_BYTES = 32 * T::CPR * 16;
+  // PV A operand (V^T) via ds_read_b64_tr_b16: within each 16-lane group g,
+  // lane 4e + r supplies the address of V[key_e][d0 + 4r .. +3]; the read
+  // returns to lane i of the group the 4 keys key_0..3 of column d0 + i.
+  // key_e = 16*s + 8*(g/2) + 4*half + e: the V swizzle depends on key % 4 = e
+  // only, so s and half add constants.
+  const int g16 = lane >> 4, e4 = (lane & 15) >> 2, r4 = lane & 3;
+  int v_rd[T::DBLK];
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b) {
+    const int d = 32 * b + 16 * (g16 & 1) + 4 * r4;
+    v_rd[b] = v_chunk_off<D>(8 * (g16 >> 1) + e4, d >> 3) + 2 * (d & 7);
+  }
+  constexpr int V_KEY_BYTES = T::CPR * 16;
+
+  floatx16 sacc[T::KB];   // S_j^T, then P_j in fp32
+  half8 pf[T::PSTEPS];    // P_j^T in fp16: B operand of PV_j
+
+  // T stage for key tile j: S^T = K_j Q^T.
+  auto qk = [&](auto slot) __attribute__((always_inline)) {
+    const lds_char* ks = k_ring + slot * T::TILE_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < T::KSTEPS; ++s) {
-        const half8 a = *reinterpret_cast<const half8*>(ks + (32 * kb + l32) * T::K_STRIDE + 16 * s + 8 * hh);
+    for (int s = 0; s < T::KSTEPS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const half8 a = *(const lds_half8*)(ks + k_rd[s] + kb * K_BLOCK_BYTES);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], sacc[kb], 0, 0, 0);
       }
-    }
-
-    // mask keys past N (ragged tail) and, if causal, keys after the query
-    const bool need_mask = (j0 + T::BN > N) || (CAUSAL && j0 + T::BN - 1 > wave_q_lo);
-    if (need_mask) {
+  };
+  // U stage for key tile j: O^T += V_j^T P_j^T.
+  auto pv = [&](auto slot) __attribute__((always_inline)) {
+    const lds_char* vs = v_ring + slot * T::TILE_BYTES;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < T::PSTEPS; ++s)
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b) {
+        const lds_char* a0 = vs + v_rd[b] + 16 * s * V_KEY_BYTES;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)a0);
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(a0 + 4 * V_KEY_BYTES));
+        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[b], 0, 0, 0);
+      }
+  };
+
+  const float c2 = p.scale_log2;
+  const half2 ones = {(_Float16)1.f, (_Float16)1.f};
+
+  // C stage for key tile j: mask, online softmax in base 2, P_j -> fp16.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int j0 = j * T::BN;
+    // keys past N (ragged tail) and, if causal, keys after the query
+    if ((j0 + T::BN > N) || (CAUSAL && j0 + T::BN - 1 > wave_q_lo)) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
           if (key >= N || (CAUSAL && key > qrow)) sacc[kb][i] = -INFINITY;
         }
     }
-
-    // C stage: online softmax in base 2
-    float mx = sacc[0][0];
+    float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float rs = 0.f;
-    half8 pf[T::PSTEPS];
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    const float m_tile = max_halves(mx) * c2;
+    // The reference max moves only when some row's max grows by more than
+    // 2^RESCALE_LOG2. Until then p <= 2^RESCALE_LOG2; O and l share the same
+    // reference, so O / l is unchanged and the rescale of O is skipped.
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -m_new));
-        rs += e;
-        pf[2 * kb + (i >> 3)][i & 7] = (_Float16)e;
-      }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < T::DBLK; ++b) oacc[b] *= alpha;
-
-    // U stage: O^T += V^T P^T
-#pragma unroll
-    for (int b = 0; b < T::DBLK; ++b)
-#pragma unroll
-      for (int s = 0; s < T::PSTEPS; ++s) {
-        const half8 a = *reinterpret_cast<const half8*>(vt + (32 * b + l32) * T::VT_STRIDE + 16 * s + 8 * hh);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[b], 0, 0, 0);
-      }
-
-    // producer: stage tile j+1 into the other slot, fetch tile j+2
-    if (j + 1 < n_kv) {
-      stage((j + 1) & 1);
-      if (j + 2 < n_kv) fetch(j + 2);
+      for (int b = 0; b < T::DBLK; ++b) oacc[b] *= alpha;
     }
-    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pf[2 * kb + (i >> 3)][i & 7] =
+            (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -m_run));
+    // row sum of the fp16 weights that multiply V, accumulated in fp32
+    float rs[T::PSTEPS];
+#pragma unroll
+    for (int s = 0; s < T::PSTEPS; ++s) {
+      rs[s] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2 pp = {pf[s][2 * e], pf[s][2 * e + 1]};
+        rs[s] = __builtin_amdgcn_fdot2(pp, ones, rs[s], false);
+      }
+    }
+    float rsum = rs[0];
+#pragma unroll
+    for (int s = 1; s < T::PSTEPS; ++s) rsum += rs[s];
+    l_run += rsum;
+  };
+
+  // ---- ping-pong schedule -------------------------------------------------------
+  // Every wave runs the same sequence of barrier-separated local intervals:
+  // 2j = matrix-core phase of iteration j (U_{j-1}, T_j), 2j+1 = vector phase
+  // (C_j). Group 1 starts one interval late (an extra barrier up front, which
+  // group 0 matches at the end), so in every interval one wave of each SIMD
+  // feeds the matrix core while the other runs the softmax.
+  //
+  // Rings (slot = tile % 3): K_j is read in global intervals 2j .. 2j+1, V_j
+  // in 2j+2 .. 2j+3. Each wave loads V_{j+1} at the start of local interval
+  // 2j and K_{j+2} at the start of local interval 2j+1; the slots they fill
+  // held V_{j-2} and K_{j-1}, which both groups have finished with. At the
+  // end of each local interval 2j a wave waits for its own K_{j+1} and V_j
+  // loads; the barrier after that precedes their first read. Loads past the
+  // sequence end return zeros into slots that are never read.
+  auto wait_and_sync = [&]() __attribute__((always_inline)) {
+    // this wave's K_{j+1} and V_j loads landed (V_{j+1} may be in flight)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
+  };
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+
+  // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
+  // compile time, so every LDS operand address is a lane register plus an
+  // immediate.
+  auto steady = [&](int j, auto u_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
+    constexpr int PREV = (U + 2) % 3;
+    // local interval 2j: matrix core
+    fetch(rv, v_ring, v_src, j + 1);
+    __builtin_amdgcn_s_setprio(1);
+    pv(std::integral_constant<int, PREV>{});
+    qk(std::integral_constant<int, U>{});
+    // operand reads run about 4 MFMAs ahead of their MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, T::LOADS_PER_WAVE, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < T::PSTEPS * T::DBLK - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 + T::KSTEPS * T::KB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_s_setprio(0);
+    wait_and_sync();
+    // local interval 2j+1: vector ALU
+    fetch(rk, k_ring, k_src, j + 2);
+    softmax(j);
+    sync();
+  };
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+
+  fetch(rk, k_ring, k_src, 0);
+  fetch(rv, v_ring, v_src, 0);
+  fetch(rk, k_ring, k_src, 1);
+  // K_0 landed (V_0 and K_1 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
+  if (group == 1) sync();
+
+  // j = 0: T_0, then C_0
+  fetch(rv, v_ring, v_src, 1);
+  if (n_wave > 0) qk(U0{});
+  wait_and_sync();
+  fetch(rk, k_ring, k_src, 2);
+  if (n_wave > 0) softmax(0);
+  sync();
+  // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
+  int j = 1;
+  for (; j + 3 <= n_wave; j += 3) {
+    steady(j, U1{});
+    steady(j + 1, U2{});
+    steady(j + 2, U0{});
   }
+  if (j < n_wave) {
+    steady(j, U1{});
+    ++j;
+    if (j < n_wave) {
+      steady(j, U2{});
+      ++j;
+    }
+  }
+  // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
+  // which the wave still loads its share of the workgroup's tiles
+  for (; j <= n_kv; ++j) {
+    fetch(rv, v_ring, v_src, j + 1);
+    if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
+    wait_and_sync();
+    fetch(rk, k_ring, k_src, j + 2);
+    sync();
+  }
+  if (group == 0) sync();
+  // no LDS-DMA load may still be writing when the workgroup exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2 -------------------
   const float l_tot = sum_halves(l_run);
