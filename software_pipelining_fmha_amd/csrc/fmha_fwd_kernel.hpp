@@ -66,9 +66,15 @@ struct Tile {
   static constexpr int DBLK = D / 32;           // 32-row blocks of O^T
   static constexpr int PSTEPS = BN / 16;        // MFMA k-steps of PV
   static constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
-  static constexpr int SLOTS = 3;               // ring depth for K and for V
-  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
+  static constexpr int TILE_BYTES = BN * D * 2; // one K tile in LDS
+  static constexpr int VT_STRIDE = BN * 2 + 16; // bytes per d row of a V^T tile (16-byte pad)
+  static constexpr int VT_BYTES = D * VT_STRIDE;  // one V^T tile in LDS
+  static constexpr int SLOTS = 3;               // ring depth for K and for V^T
+  static constexpr int LDS_BYTES = SLOTS * (TILE_BYTES + VT_BYTES);
+  // V staging: each wave moves keys 8w .. 8w+7 of a tile; each lane 2 d columns
+  static constexpr int V_KEYS_PER_WAVE = BN / WAVES;
+  static constexpr int V_COLS = D / 64;          // d columns per lane (1 or 2)
+  static_assert(V_KEYS_PER_WAVE == 8 && V_COLS * 64 == D, "V staging covers the tile");
   // one tile = TILE_BYTES / 1024 wave-wide 16-byte-per-lane LDS-DMA loads
   static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;  // per tile
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) half8 lds_half8;
   typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  // LDS: a 3-slot ring of K tiles and a 3-slot ring of V tiles.
+  // LDS: a 3-slot ring of K tiles and a 3-slot ring of V^T tiles.
   __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
@@ -192,26 +198,53 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // Tiles this wave computes: causal rows see no key past wave_q_lo + 31.
   const int n_wave = CAUSAL ? min(n_kv, (wave_q_lo + T::QW - 1) / T::BN + 1) : n_kv;
 
-  // ---- producer: HBM -> LDS ring slot, no VGPR staging -----------------------
-  // Wave w issues LDS-DMA loads w*LOADS_PER_WAVE .. +LOADS_PER_WAVE-1 of a
-  // tile; load i fills the tile's LDS chunks 64*i .. 64*i+63 (one per lane),
-  // and each lane fetches the global chunk that the swizzled layout puts there.
-  int k_src[T::LOADS_PER_WAVE], v_src[T::LOADS_PER_WAVE];
+  // ---- producers ---------------------------------------------------------------
+  // K: HBM -> LDS ring slot by LDS-DMA, no register staging. Wave w issues
+  // loads w*LOADS_PER_WAVE .. +LOADS_PER_WAVE-1 of a tile; load i fills the
+  // tile's LDS chunks 64*i .. 64*i+63 (one per lane), and each lane fetches
+  // the global chunk that the swizzled layout puts there.
+  int k_src[T::LOADS_PER_WAVE];
 #pragma unroll
   for (int r = 0; r < T::LOADS_PER_WAVE; ++r) {
     const int x = 64 * (wave * T::LOADS_PER_WAVE + r) + lane;  // LDS chunk index
     const int row = x / T::CPR, slot = x % T::CPR;
-    const int kc = slot ^ (row % T::CPR);
-    k_src[r] = (key_of_row(row) * D + 8 * kc) * 2;
-    const int vc = slot ^ ((4 * (row & 3)) % T::CPR);
-    v_src[r] = (row * D + 8 * vc) * 2;
+    k_src[r] = (key_of_row(row) * D + 8 * (slot ^ (row % T::CPR))) * 2;
   }
-  auto fetch = [&](const __amdgpu_buffer_rsrc_t& r, lds_char* ring, const int (&src)[T::LOADS_PER_WAVE],
-                   int j) __attribute__((always_inline)) {
-    lds_char* dst = ring + (j % T::SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
+  auto fetch_k = [&](int j, int slot) __attribute__((always_inline)) {
+    lds_char* dst = k_ring + slot * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
 #pragma unroll
     for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
-      load16_to_lds(r, j * T::BN * D * 2 + src[i], dst + i * 1024);
+      load16_to_lds(rk, j * T::BN * D * 2 + k_src[i], dst + i * 1024);
+  };
+  // V: HBM -> registers (keys 8w .. 8w+7 of the tile, d columns
+  // V_COLS*lane .. +V_COLS-1), transposed in registers and written to a V^T
+  // tile ([d][key], rows padded to VT_STRIDE bytes). The loads are coalesced
+  // (a wave reads whole key rows); the A operand of PV is then one
+  // ds_read_b128 of 8 consecutive keys of one d row.
+  uint32_t vreg[T::V_KEYS_PER_WAVE];
+  const int v_src = ((T::V_KEYS_PER_WAVE * wave) * D + T::V_COLS * lane) * 2;
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < T::V_KEYS_PER_WAVE; ++r) {
+      const int off = v_src + (j * T::BN + r) * D * 2;
+      if constexpr (T::V_COLS == 2)
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+      else
+        vreg[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
+    }
+  };
+  auto store_vt = [&](int slot) __attribute__((always_inline)) {
+    lds_char* vt = v_ring + slot * T::VT_BYTES + (T::V_COLS * lane) * T::VT_STRIDE +
+                   T::V_KEYS_PER_WAVE * wave * 2;
+#pragma unroll
+    for (int c = 0; c < T::V_COLS; ++c) {
+      // key pairs (2i, 2i+1) of column c: half c of each loaded dword
+      const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;
+      intx4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (int)__builtin_amdgcn_perm(vreg[2 * i + 1], vreg[2 * i], sel);
+      *(__attribute__((address_space(3))) intx4*)(vt + c * T::VT_STRIDE) = w;
+    }
   };
 
   // ---- consumer-side LDS offsets (per lane, constant over the loop) ----------
@@ -222,19 +255,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
 #pragma unroll
   for (int s = 0; s < T::KSTEPS; ++s) k_rd[s] = k_chunk_off<D>(l32, 2 * s + hh);
   constexpr int K_BLOCK_BYTES = 32 * T::CPR * 16;
-  // PV A operand (V^T) via ds_read_b64_tr_b16: within each 16-lane group g,
-  // lane 4e + r supplies the address of V[key_e][d0 + 4r .. +3]; the read
-  // returns to lane i of the group the 4 keys key_0..3 of column d0 + i.
-  // key_e = 16*s + 8*(g/2) + 4*half + e: the V swizzle depends on key % 4 = e
-  // only, so s and half add constants.
-  const int g16 = lane >> 4, e4 = (lane & 15) >> 2, r4 = lane & 3;
-  int v_rd[T::DBLK];
-#pragma unroll
-  for (int b = 0; b < T::DBLK; ++b) {
-    const int d = 32 * b + 16 * (g16 & 1) + 4 * r4;
-    v_rd[b] = v_chunk_off<D>(8 * (g16 >> 1) + e4, d >> 3) + 2 * (d & 7);
-  }
-  constexpr int V_KEY_BYTES = T::CPR * 16;
+  // PV A operand: V^T row 32*b + l32, keys 16*s + 8*hh .. +7 (16 bytes).
+  const int vt_rd = l32 * T::VT_STRIDE + 16 * hh;
 
   floatx16 sacc[T::KB];   // S_j^T, then P_j in fp32
   half8 pf[T::PSTEPS];    // P_j^T in fp16: B operand of PV_j
@@ -256,15 +278,12 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   };
   // U stage for key tile j: O^T += V_j^T P_j^T.
   auto pv = [&](auto slot) __attribute__((always_inline)) {
-    const lds_char* vs = v_ring + slot * T::TILE_BYTES;
+    const lds_char* vs = v_ring + slot * T::VT_BYTES + vt_rd;
 #pragma unroll
     for (int s = 0; s < T::PSTEPS; ++s)
 #pragma unroll
       for (int b = 0; b < T::DBLK; ++b) {
-        const lds_char* a0 = vs + v_rd[b] + 16 * s * V_KEY_BYTES;
-        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)a0);
-        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(a0 + 4 * V_KEY_BYTES));
-        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const half8 a = *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * s);
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[b], 0, 0, 0);
       }
   };
@@ -328,22 +347,33 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // ---- ping-pong schedule -------------------------------------------------------
   // Every wave runs the same sequence of barrier-separated local intervals:
   // 2j = matrix-core phase of iteration j (U_{j-1}, T_j), 2j+1 = vector phase
-  // (C_j). Group 1 starts one interval late (an extra barrier up front, which
-  // group 0 matches at the end), so in every interval one wave of each SIMD
-  // feeds the matrix core while the other runs the softmax.
+  // (write V^T_{j+1}, issue the loads of K_{j+2} and V_{j+2}, C_j). Group 1
+  // starts one interval late (an extra barrier up front, which group 0
+  // matches at the end), so in every interval one wave of each SIMD feeds
+  // the matrix core while the other runs the vector work.
   //
-  // Rings (slot = tile % 3): K_j is read in global intervals 2j .. 2j+1, V_j
-  // in 2j+2 .. 2j+3. Each wave loads V_{j+1} at the start of local interval
-  // 2j and K_{j+2} at the start of local interval 2j+1; the slots they fill
-  // held V_{j-2} and K_{j-1}, which both groups have finished with. At the
-  // end of each local interval 2j a wave waits for its own K_{j+1} and V_j
-  // loads; the barrier after that precedes their first read. Loads past the
-  // sequence end return zeros into slots that are never read.
-  auto wait_and_sync = [&]() __attribute__((always_inline)) {
-    // this wave's K_{j+1} and V_j loads landed (V_{j+1} may be in flight)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
-  };
+  // Rings (slot = tile % 3). K_j is read in global intervals 2j .. 2j+1 and
+  // V^T_j in 2j+2 .. 2j+3. K_{j+2} is DMA'd and V^T_{j+1} written in local
+  // interval 2j+1 (global 2j+1 or 2j+2); the slots held K_{j-1} and V^T_{j-2},
+  // whose last reads were in global 2j-1 and 2j-3. A wave waits for its K_{j+1}
+  // DMA at the end of local interval 2j, and for its V^T writes (lgkmcnt) at
+  // the end of each vector interval; the barrier after each wait precedes the
+  // first read. Loads past the sequence end return zeros into slots that are
+  // never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+  auto mfma_sync = [&]() __attribute__((always_inline)) {
+    // this wave's DMA of K_{j+1} landed (its V_{j+1} register loads may not have)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
+  };
+  auto vector_sync = [&]() __attribute__((always_inline)) {
+    // this wave's V^T writes are in LDS
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto produce = [&](int j) __attribute__((always_inline)) {
+    store_vt((j + 1) % T::SLOTS);
+    fetch_k(j + 2, (j + 2) % T::SLOTS);
+    load_v(j + 2);
+  };
 
   // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
   // compile time, so every LDS operand address is a lane register plus an
@@ -352,49 +382,43 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     constexpr int U = decltype(u_tag)::value;
     constexpr int PREV = (U + 2) % 3;
     // local interval 2j: matrix core
-    fetch(rv, v_ring, v_src, j + 1);
     __builtin_amdgcn_s_setprio(1);
     pv(std::integral_constant<int, PREV>{});
     qk(std::integral_constant<int, U>{});
     // operand reads run about 4 MFMAs ahead of their MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, T::LOADS_PER_WAVE, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < T::PSTEPS * T::DBLK - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4 + T::KSTEPS * T::KB - 4; ++i) {
+    for (int i = 0; i < T::PSTEPS * T::DBLK + T::KSTEPS * T::KB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
-    wait_and_sync();
+    mfma_sync();
     // local interval 2j+1: vector ALU
-    fetch(rk, k_ring, k_src, j + 2);
+    produce(j);
     softmax(j);
-    sync();
+    vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
   using U1 = std::integral_constant<int, 1>;
   using U2 = std::integral_constant<int, 2>;
 
-  fetch(rk, k_ring, k_src, 0);
-  fetch(rv, v_ring, v_src, 0);
-  fetch(rk, k_ring, k_src, 1);
-  // K_0 landed (V_0 and K_1 may still be in flight)
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
+  fetch_k(0, 0);
+  fetch_k(1, 1);
+  load_v(0);
+  store_vt(0);
+  load_v(1);
+  // K_0, K_1 landed and V^T_0 written (V_1 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
   if (group == 1) sync();
 
   // j = 0: T_0, then C_0
-  fetch(rv, v_ring, v_src, 1);
   if (n_wave > 0) qk(U0{});
-  wait_and_sync();
-  fetch(rk, k_ring, k_src, 2);
+  mfma_sync();
+  produce(0);
   if (n_wave > 0) softmax(0);
-  sync();
+  vector_sync();
   // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
   int j = 1;
   for (; j + 3 <= n_wave; j += 3) {
@@ -411,16 +435,15 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     }
   }
   // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
-  // which the wave still loads its share of the workgroup's tiles
+  // which the wave still produces its share of the workgroup's tiles
   for (; j <= n_kv; ++j) {
-    fetch(rv, v_ring, v_src, j + 1);
     if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
-    wait_and_sync();
-    fetch(rk, k_ring, k_src, j + 2);
-    sync();
+    mfma_sync();
+    produce(j);
+    vector_sync();
   }
   if (group == 0) sync();
-  // no LDS-DMA load may still be writing when the workgroup exits
+  // no load may still be in flight when the workgroup exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2 -------------------
