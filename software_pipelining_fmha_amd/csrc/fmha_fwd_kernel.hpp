@@ -291,8 +291,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   const float c2 = p.scale_log2;
   const half2 ones = {(_Float16)1.f, (_Float16)1.f};
 
-  // C stage for key tile j: mask, online softmax in base 2, P_j -> fp16.
-  auto softmax = [&](int j) __attribute__((always_inline)) {
+  // C stage, first half, for key tile j: mask, row max, lazy rescale and
+  // p = 2^(s*c2 - m) in place (fp32).
+  auto softmax_exp = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * T::BN;
     // keys past N (ragged tail) and, if causal, keys after the query
     if ((j0 + T::BN > N) || (CAUSAL && j0 + T::BN - 1 > wave_q_lo)) {
@@ -312,7 +313,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     const float m_tile = max_halves(mx) * c2;
     // The reference max moves only when some row's max grows by more than
     // 2^RESCALE_LOG2. Until then p <= 2^RESCALE_LOG2; O and l share the same
-    // reference, so O / l is unchanged and the rescale of O is skipped.
+    // reference, so O / l is unchanged and the rescale of O is skipped. O and l
+    // already hold every earlier tile here (U_{j-1} ran before C_j).
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -324,13 +326,16 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pf[2 * kb + (i >> 3)][i & 7] =
-            (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -m_run));
-    // row sum of the fp16 weights that multiply V, accumulated in fp32
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -m_run));
+  };
+  // C stage, second half: P -> fp16 (the B operand of U) and its row sum.
+  // The row sum adds the same fp16 weights that multiply V, in fp32.
+  auto softmax_pack = [&]() __attribute__((always_inline)) {
     float rs[T::PSTEPS];
 #pragma unroll
     for (int s = 0; s < T::PSTEPS; ++s) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[s][i] = (_Float16)sacc[s >> 1][8 * (s & 1) + i];
       rs[s] = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -345,34 +350,33 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   };
 
   // ---- ping-pong schedule -------------------------------------------------------
-  // Every wave runs the same sequence of barrier-separated local intervals:
-  // 2j = matrix-core phase of iteration j (U_{j-1}, T_j), 2j+1 = vector phase
-  // (write V^T_{j+1}, issue the loads of K_{j+2} and V_{j+2}, C_j). Group 1
+  // Every wave runs the same sequence of barrier-separated local intervals.
+  // 2j is the matrix-core interval of iteration j: P_{j-1} -> fp16 and its row
+  // sum, U_{j-1}, T_j, and the producer work (write V^T_j, DMA K_{j+2}, load
+  // V_{j+1}), all vector work that issues between the MFMAs. 2j+1 is the vector
+  // interval: the first half of C_j (mask, max, lazy rescale, exp2). Group 1
   // starts one interval late (an extra barrier up front, which group 0
   // matches at the end), so in every interval one wave of each SIMD feeds
-  // the matrix core while the other runs the vector work.
+  // the matrix core while the other runs the exponentials.
   //
   // Rings (slot = tile % 3). K_j is read in global intervals 2j .. 2j+1 and
-  // V^T_j in 2j+2 .. 2j+3. K_{j+2} is DMA'd and V^T_{j+1} written in local
-  // interval 2j+1 (global 2j+1 or 2j+2); the slots held K_{j-1} and V^T_{j-2},
-  // whose last reads were in global 2j-1 and 2j-3. A wave waits for its K_{j+1}
-  // DMA at the end of local interval 2j, and for its V^T writes (lgkmcnt) at
-  // the end of each vector interval; the barrier after each wait precedes the
-  // first read. Loads past the sequence end return zeros into slots that are
-  // never read.
+  // V^T_j in 2j+2 .. 2j+3. In local interval 2j a wave writes V^T_j (global
+  // 2j or 2j+1) over V^T_{j-3}, last read in 2j-3, and DMAs K_{j+2} over
+  // K_{j-1}, last read in 2j-1. At the end of local interval 2j a wave waits
+  // for its K_{j+1} DMA and its V^T_j writes; the barrier after the wait
+  // precedes their first reads (global 2j+2). Loads past the sequence end
+  // return zeros into slots that are never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
-    // this wave's DMA of K_{j+1} landed (its V_{j+1} register loads may not have)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
-  };
-  auto vector_sync = [&]() __attribute__((always_inline)) {
-    // this wave's V^T writes are in LDS
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // K_{j+1} DMA landed (this interval's K_{j+2} and V_{j+1} loads may not
+    // have); V^T_j writes are in LDS
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE + T::V_KEYS_PER_WAVE)
+                 : "memory");
   };
   auto produce = [&](int j) __attribute__((always_inline)) {
-    store_vt((j + 1) % T::SLOTS);
+    store_vt(j % T::SLOTS);
     fetch_k(j + 2, (j + 2) % T::SLOTS);
-    load_v(j + 2);
+    load_v(j + 1);
   };
 
   // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
@@ -383,22 +387,24 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     constexpr int PREV = (U + 2) % 3;
     // local interval 2j: matrix core
     __builtin_amdgcn_s_setprio(1);
+    softmax_pack();
     pv(std::integral_constant<int, PREV>{});
     qk(std::integral_constant<int, U>{});
-    // operand reads run about 4 MFMAs ahead of their MFMA
+    produce(j);
+    // operand reads run about 4 MFMAs ahead of their MFMA; vector work between
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < T::PSTEPS * T::DBLK + T::KSTEPS * T::KB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     // local interval 2j+1: vector ALU
-    produce(j);
-    softmax(j);
-    vector_sync();
+    softmax_exp(j);
+    sync();
   };
   using U0 = std::integral_constant<int, 0>;
   using U1 = std::integral_constant<int, 1>;
@@ -407,19 +413,17 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   fetch_k(0, 0);
   fetch_k(1, 1);
   load_v(0);
-  store_vt(0);
-  load_v(1);
-  // K_0, K_1 landed and V^T_0 written (V_1 may still be in flight)
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
+  // K_0 landed (K_1 and V_0 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE + T::V_KEYS_PER_WAVE) : "memory");
   if (group == 1) sync();
 
   // j = 0: T_0, then C_0
   if (n_wave > 0) qk(U0{});
-  mfma_sync();
   produce(0);
-  if (n_wave > 0) softmax(0);
-  vector_sync();
-  // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
+  mfma_sync();
+  if (n_wave > 0) softmax_exp(0);
+  sync();
+  // 1 <= j < n_wave: P_{j-1}, U_{j-1}, T_j, then C_j
   int j = 1;
   for (; j + 3 <= n_wave; j += 3) {
     steady(j, U1{});
@@ -437,10 +441,13 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
   // which the wave still produces its share of the workgroup's tiles
   for (; j <= n_kv; ++j) {
-    if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
-    mfma_sync();
+    if (j == n_wave && j >= 1) {
+      softmax_pack();
+      pv((j - 1) % T::SLOTS);
+    }
     produce(j);
-    vector_sync();
+    mfma_sync();
+    sync();
   }
   if (group == 0) sync();
   // no load may still be in flight when the workgroup exits
