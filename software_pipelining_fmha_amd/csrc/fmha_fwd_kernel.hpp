@@ -352,31 +352,33 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // ---- ping-pong schedule -------------------------------------------------------
   // Every wave runs the same sequence of barrier-separated local intervals.
   // 2j is the matrix-core interval of iteration j: P_{j-1} -> fp16 and its row
-  // sum, U_{j-1}, T_j, and the producer work (write V^T_j, DMA K_{j+2}, load
-  // V_{j+1}), all vector work that issues between the MFMAs. 2j+1 is the vector
-  // interval: the first half of C_j (mask, max, lazy rescale, exp2). Group 1
-  // starts one interval late (an extra barrier up front, which group 0
-  // matches at the end), so in every interval one wave of each SIMD feeds
-  // the matrix core while the other runs the exponentials.
+  // sum (vector work that issues between the MFMAs), U_{j-1}, T_j. 2j+1 is the
+  // vector interval: the producer work (write V^T_{j+1}, DMA K_{j+2}, load
+  // V_{j+2}) and the first half of C_j (mask, max, lazy rescale, exp2).
+  // Group 1 starts one interval late (an extra barrier up front, which group 0
+  // matches at the end), so in every interval one wave of each SIMD feeds the
+  // matrix core while the other runs the vector work.
   //
   // Rings (slot = tile % 3). K_j is read in global intervals 2j .. 2j+1 and
-  // V^T_j in 2j+2 .. 2j+3. In local interval 2j a wave writes V^T_j (global
-  // 2j or 2j+1) over V^T_{j-3}, last read in 2j-3, and DMAs K_{j+2} over
-  // K_{j-1}, last read in 2j-1. At the end of local interval 2j a wave waits
-  // for its K_{j+1} DMA and its V^T_j writes; the barrier after the wait
-  // precedes their first reads (global 2j+2). Loads past the sequence end
-  // return zeros into slots that are never read.
+  // V^T_j in 2j+2 .. 2j+3. In local interval 2j+1 a wave writes V^T_{j+1}
+  // (global 2j+1 or 2j+2) over V^T_{j-2}, last read in 2j-1, and DMAs K_{j+2}
+  // over K_{j-1}, last read in 2j-1. A wave waits for its K_{j+1} DMA at the end
+  // of local interval 2j and for its V^T writes at the end of each vector
+  // interval; the barrier after each wait precedes the first read. Loads past
+  // the sequence end return zeros into slots that are never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
-    // K_{j+1} DMA landed (this interval's K_{j+2} and V_{j+1} loads may not
-    // have); V^T_j writes are in LDS
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE + T::V_KEYS_PER_WAVE)
-                 : "memory");
+    // this wave's K_{j+1} DMA landed (its V_{j+1} register loads may not have)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
+  };
+  auto vector_sync = [&]() __attribute__((always_inline)) {
+    // this wave's V^T writes are in LDS
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto produce = [&](int j) __attribute__((always_inline)) {
-    store_vt(j % T::SLOTS);
+    store_vt((j + 1) % T::SLOTS);
     fetch_k(j + 2, (j + 2) % T::SLOTS);
-    load_v(j + 1);
+    load_v(j + 2);
   };
 
   // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
@@ -390,21 +392,22 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     softmax_pack();
     pv(std::integral_constant<int, PREV>{});
     qk(std::integral_constant<int, U>{});
-    produce(j);
-    // operand reads run about 4 MFMAs ahead of their MFMA; vector work between
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // Operand reads run 6 MFMAs ahead of their MFMA, with one vector
+    // instruction of the P packing between consecutive MFMAs.
+    constexpr int AHEAD = 6;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < T::PSTEPS * T::DBLK + T::KSTEPS * T::KB - 4; ++i) {
+    for (int i = 0; i < T::PSTEPS * T::DBLK + T::KSTEPS * T::KB - AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     // local interval 2j+1: vector ALU
+    produce(j);
     softmax_exp(j);
-    sync();
+    vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
   using U1 = std::integral_constant<int, 1>;
@@ -413,16 +416,18 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   fetch_k(0, 0);
   fetch_k(1, 1);
   load_v(0);
-  // K_0 landed (K_1 and V_0 may still be in flight)
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE + T::V_KEYS_PER_WAVE) : "memory");
+  store_vt(0);
+  load_v(1);
+  // K_0, K_1 landed and V^T_0 written (V_1 may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
   if (group == 1) sync();
 
   // j = 0: T_0, then C_0
   if (n_wave > 0) qk(U0{});
-  produce(0);
   mfma_sync();
+  produce(0);
   if (n_wave > 0) softmax_exp(0);
-  sync();
+  vector_sync();
   // 1 <= j < n_wave: P_{j-1}, U_{j-1}, T_j, then C_j
   int j = 1;
   for (; j + 3 <= n_wave; j += 3) {
@@ -445,9 +450,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
       softmax_pack();
       pv((j - 1) % T::SLOTS);
     }
-    produce(j);
     mfma_sync();
-    sync();
+    produce(j);
+    vector_sync();
   }
   if (group == 0) sync();
   // no load may still be in flight when the workgroup exits
