@@ -1,8 +1,8 @@
 // Fused multi-head attention forward pass for gfx950 (MI355X, CDNA4).
 //
 // One workgroup owns one (batch, head, query tile). The query tile stays in
-// VGPRs for the whole kernel. Key/value tiles stream from HBM through a
-// double-buffered LDS ring. Each pages' stage maps onto gfx950 units:
+// VGPRs for the whole kernel. Key/value tiles stream from HBM into LDS rings
+// by LDS-DMA. Each stage of the pages maps onto gfx950 units:
 // - T stage, S = Q K^T (Tawa, section III-D): fp16 MFMA, fp32 accumulate;
 // - C stage, online softmax with rescale (PipeThreader's softmax and
 //   rescale tasks): VALU, exp2 on the transcendental unit;
@@ -20,6 +20,8 @@
 //   they are the B operand of O^T += V^T P^T, with no shuffle.
 // * V is stored transposed in LDS ([d][key], keys contiguous). One 16-byte
 //   LDS read then yields the matching A operand (8 keys of one d column).
+//   The transpose happens LDS to LDS: V arrives in natural layout and
+//   ds_read_b64_tr_b16 returns it column-wise.
 // * O^T accumulates with one query per lane column. The per-row rescale
 //   factor is therefore a per-lane scalar.
 #pragma once
@@ -40,7 +42,11 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
 // Reference-max slack (base 2) before O and l are rescaled.
 constexpr float RESCALE_LOG2 = 8.0f;
-
+// Largest per-lane sum of one tile's weights accepted without a row max.
+// Every weight is then at most this bound, well inside the fp16 range.
+constexpr float WEIGHT_BOUND = 4096.0f;
+// MFMA slots by which an LDS operand read precedes its MFMA.
+constexpr int OPERAND_AHEAD = 4;
 
 struct Params {
   const _Float16* q;
@@ -70,11 +76,12 @@ struct Tile {
   static constexpr int VT_STRIDE = BN * 2 + 16; // bytes per d row of a V^T tile (16-byte pad)
   static constexpr int VT_BYTES = D * VT_STRIDE;  // one V^T tile in LDS
   static constexpr int SLOTS = 3;               // ring depth for K and for V^T
-  static constexpr int LDS_BYTES = SLOTS * (TILE_BYTES + VT_BYTES);
-  // V staging: each wave moves keys 8w .. 8w+7 of a tile; each lane 2 d columns
+  static constexpr int STAGE_SLOTS = 3;         // ring depth for V tiles in natural layout
+  static constexpr int LDS_BYTES = SLOTS * (TILE_BYTES + VT_BYTES) + STAGE_SLOTS * TILE_BYTES;
+  // V^T production: wave w writes keys 8w .. 8w+7 of d rows lane + 64*h
   static constexpr int V_KEYS_PER_WAVE = BN / WAVES;
-  static constexpr int V_COLS = D / 64;          // d columns per lane (1 or 2)
-  static_assert(V_KEYS_PER_WAVE == 8 && V_COLS * 64 == D, "V staging covers the tile");
+  static constexpr int V_COLS = D / 64;          // d rows per lane (1 or 2)
+  static_assert(V_KEYS_PER_WAVE == 8 && V_COLS * 64 == D, "V^T production covers the tile");
   // one tile = TILE_BYTES / 1024 wave-wide 16-byte-per-lane LDS-DMA loads
   static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;  // per tile
@@ -127,26 +134,16 @@ __device__ __forceinline__ int k_chunk_off(int p, int c) {
   return (p * CPR + (c ^ (p % CPR))) * 16;
 }
 
-// LDS byte offset of 16-byte chunk c of key row `key` in a V tile (row-major,
-// d contiguous). The swizzle 4*(key%4) makes the transposed 8-byte reads of
-// 4 consecutive keys x 4 chunks (one ds_read_b64_tr_b16 half-wave) hit 16
-// distinct bank groups.
-template <int D>
-__device__ __forceinline__ int v_chunk_off(int key, int c) {
-  constexpr int CPR = D / 8;
-  return (key * CPR + (c ^ ((4 * (key & 3)) % CPR))) * 16;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p) {
   using T = Tile<D>;
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) half8 lds_half8;
-  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  // LDS: a 3-slot ring of K tiles and a 3-slot ring of V^T tiles.
+  // LDS: 3-slot rings of K tiles, of V^T tiles and of V tiles (natural layout).
   __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
+  lds_char* const v_stage = v_ring + T::SLOTS * T::VT_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,34 +213,66 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
       load16_to_lds(rk, j * T::BN * D * 2 + k_src[i], dst + i * 1024);
   };
-  // V: HBM -> registers (keys 8w .. 8w+7 of the tile, d columns
-  // V_COLS*lane .. +V_COLS-1), transposed in registers and written to a V^T
-  // tile ([d][key], rows padded to VT_STRIDE bytes). The loads are coalesced
-  // (a wave reads whole key rows); the A operand of PV is then one
-  // ds_read_b128 of 8 consecutive keys of one d row.
-  uint32_t vreg[T::V_KEYS_PER_WAVE];
-  const int v_src = ((T::V_KEYS_PER_WAVE * wave) * D + T::V_COLS * lane) * 2;
-  auto load_v = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < T::V_KEYS_PER_WAVE; ++r) {
-      const int off = v_src + (j * T::BN + r) * D * 2;
-      if constexpr (T::V_COLS == 2)
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
-      else
-        vreg[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
-    }
+  // V: HBM -> a 3-slot staging ring in natural [key][d] layout by LDS-DMA,
+  // three tiles ahead. Chunk c of key row k is stored at chunk c ^ v_swz(k),
+  // so that the transposing reads below touch distinct banks.
+  auto v_swz = [](int row) __attribute__((always_inline)) {
+    return ((D == 128 ? 4 : 2) * (row & 3)) % T::CPR;
   };
-  auto store_vt = [&](int slot) __attribute__((always_inline)) {
-    lds_char* vt = v_ring + slot * T::VT_BYTES + (T::V_COLS * lane) * T::VT_STRIDE +
+  int v_src[T::LOADS_PER_WAVE];
+#pragma unroll
+  for (int r = 0; r < T::LOADS_PER_WAVE; ++r) {
+    const int x = 64 * (wave * T::LOADS_PER_WAVE + r) + lane;
+    const int row = x / T::CPR, pos = x % T::CPR;
+    v_src[r] = (row * D + 8 * (pos ^ v_swz(row))) * 2;
+  }
+  auto fetch_v = [&](int j) __attribute__((always_inline)) {
+    lds_char* dst = v_stage + (j % T::STAGE_SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
+      load16_to_lds(rv, j * T::BN * D * 2 + v_src[i], dst + i * 1024);
+  };
+  // Staging -> V^T ([d][key], rows padded to VT_STRIDE bytes) with
+  // ds_read_b64_tr_b16. In each 16-lane group g, source lane i reads 4
+  // d-values (d0 + 4*(i%4) ..) of key k0 + i/4, and result lane i receives
+  // d0 + i of keys k0 .. k0+3. With d0 = 64h + 16g and k0 = 8w + 4q, lane l
+  // ends with keys 8w .. 8w+7 of d row 64h + l: one 16-byte V^T store.
+  int tr_src[T::V_COLS][2];
+#pragma unroll
+  for (int h = 0; h < T::V_COLS; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = lane & 15, gq = lane >> 4;
+      const int key = T::V_KEYS_PER_WAVE * wave + 4 * q + (i >> 2);
+      const int c = 8 * h + 2 * gq + ((i & 3) >> 1);
+      tr_src[h][q] = key * D * 2 + ((c ^ v_swz(key)) * 16) + 8 * (i & 1);
+    }
+  shortx4 vtr[T::V_COLS][2];
+  auto tr_read = [&](int j) __attribute__((always_inline)) {
+    const lds_char* st = v_stage + (j % T::STAGE_SLOTS) * T::TILE_BYTES;
+#pragma unroll
+    for (int h = 0; h < T::V_COLS; ++h)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        // Inline asm: the compiler would otherwise wait for every LDS-DMA in
+        // flight (vmcnt(0)) before this read, though none targets this slot.
+        // The matching lgkmcnt wait is explicit in tr_write.
+        asm volatile("ds_read_b64_tr_b16 %0, %1"
+                     : "=v"(vtr[h][q])
+                     : "v"((uint32_t)(uintptr_t)(st + tr_src[h][q])));
+  };
+  auto tr_write = [&](int j) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_char* vt = v_ring + (j % T::SLOTS) * T::VT_BYTES + lane * T::VT_STRIDE +
                    T::V_KEYS_PER_WAVE * wave * 2;
 #pragma unroll
-    for (int c = 0; c < T::V_COLS; ++c) {
-      // key pairs (2i, 2i+1) of column c: half c of each loaded dword
-      const uint32_t sel = c == 0 ? 0x05040100u : 0x07060302u;
+    for (int h = 0; h < T::V_COLS; ++h) {
       intx4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (int)__builtin_amdgcn_perm(vreg[2 * i + 1], vreg[2 * i], sel);
-      *(__attribute__((address_space(3))) intx4*)(vt + c * T::VT_STRIDE) = w;
+      w[0] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][0], vtr[h][0], 0, 1));
+      w[1] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][0], vtr[h][0], 2, 3));
+      w[2] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][1], vtr[h][1], 0, 1));
+      w[3] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][1], vtr[h][1], 2, 3));
+      *(__attribute__((address_space(3))) intx4*)(vt + 64 * h * T::VT_STRIDE) = w;
     }
   };
 
@@ -258,7 +287,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // PV A operand: V^T row 32*b + l32, keys 16*s + 8*hh .. +7 (16 bytes).
   const int vt_rd = l32 * T::VT_STRIDE + 16 * hh;
 
-  floatx16 sacc[T::KB];   // S_j^T, then P_j in fp32
+  floatx16 sacc[T::KB];   // S_j^T (fp32)
   half8 pf[T::PSTEPS];    // P_j^T in fp16: B operand of PV_j
 
   // T stage for key tile j: S^T = K_j Q^T.
@@ -289,13 +318,11 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   };
 
   const float c2 = p.scale_log2;
-  const half2 ones = {(_Float16)1.f, (_Float16)1.f};
 
-  // C stage, first half, for key tile j: mask, row max, lazy rescale and
-  // p = 2^(s*c2 - m) in place (fp32).
-  auto softmax_exp = [&](int j) __attribute__((always_inline)) {
+  // C stage for key tile j. Keys past N (ragged tail) and, if causal, keys
+  // after the query get score -inf.
+  auto mask_tile = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * T::BN;
-    // keys past N (ragged tail) and, if causal, keys after the query
     if ((j0 + T::BN > N) || (CAUSAL && j0 + T::BN - 1 > wave_q_lo)) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
@@ -305,6 +332,33 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
           if (key >= N || (CAUSAL && key > qrow)) sacc[kb][i] = -INFINITY;
         }
     }
+  };
+  // P_j^T in fp16 (pf, the B operand of U_j) from p = 2^(s*c2 - m_run), and
+  // this lane's share of the row sum. The sum adds the fp16 weights that
+  // multiply V (v_fma_mix_f32 reads each half exactly), in fp32.
+  auto exp_pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < T::PSTEPS; ++st)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pf[st][i] = (_Float16)__builtin_amdgcn_exp2f(
+            __builtin_fmaf(sacc[st >> 1][8 * (st & 1) + i], c2, -m_run));
+    float part[T::PSTEPS];
+#pragma unroll
+    for (int st = 0; st < T::PSTEPS; ++st) {
+      const intx4 w = __builtin_bit_cast(intx4, pf[st]);
+      part[st] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // part += lo(w[e]) * 1 and part += hi(w[e]) * 1, fp16 inputs, fp32 math
+        asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(part[st]) : "v"(w[e]));
+        asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(part[st]) : "v"(w[e]));
+      }
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+  // Row max of the masked scores and the lazy rescale of O and l.
+  auto max_rescale = [&]() __attribute__((always_inline)) {
     float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -323,90 +377,125 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
 #pragma unroll
       for (int b = 0; b < T::DBLK; ++b) oacc[b] *= alpha;
     }
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c2, -m_run));
   };
-  // C stage, second half: P -> fp16 (the B operand of U) and its row sum.
-  // The row sum adds the same fp16 weights that multiply V, in fp32.
-  auto softmax_pack = [&]() __attribute__((always_inline)) {
-    float rs[T::PSTEPS];
+  // C stage with the exact tile max (the first tile of a wave).
+  auto softmax_max = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    max_rescale();
+    l_run += exp_pack();
+    asm volatile("" : "+v"(l_run));
+  };
+  // C stage for a later tile: weights against the current reference first.
+  // A lane's partial sum bounds each of its weights, so while every partial
+  // sum stays within WEIGHT_BOUND no row max is needed. Otherwise the scores,
+  // still intact, take the exact path.
+  auto softmax_fast = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    float part = exp_pack();
+    if (__builtin_amdgcn_ballot_w64(!(part <= WEIGHT_BOUND)) != 0) {
+      max_rescale();
+      part = exp_pack();
+    }
+    l_run += part;
+    asm volatile("" : "+v"(l_run));
+  };
+  // Matrix-core interval of a steady iteration: U_{j-1} (V^T slot PREV) and
+  // T_j (K slot U), 2 * NPV MFMAs in a fixed order. Even slots are U MFMAs,
+  // odd slots T MFMAs, so consecutive MFMAs never share an accumulator. Each
+  // LDS operand is read OPERAND_AHEAD slots before its MFMA; scheduling
+  // barriers keep that order, so each MFMA waits only for its own operand.
+  auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
+    constexpr int PREV = (U + 2) % 3;
+    constexpr int NPV = T::PSTEPS * T::DBLK;
+    constexpr int NM = 2 * NPV;
+    static_assert(NPV == T::KSTEPS * T::KB, "U and T MFMAs alternate");
+    constexpr int AHEAD = OPERAND_AHEAD;
+    const lds_char* ks = k_ring + U * T::TILE_BYTES;
+    const lds_char* vs = v_ring + PREV * T::VT_BYTES + vt_rd;
+    auto operand = [&](int i) __attribute__((always_inline)) {
+      const int n = i >> 1;
+      if ((i & 1) == 0) {
+        const int st = n / T::DBLK, b = n % T::DBLK;
+        return *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * st);
+      }
+      const int kb = n / T::KSTEPS, st = n % T::KSTEPS;
+      return *(const lds_half8*)(ks + k_rd[st] + kb * K_BLOCK_BYTES);
+    };
+    half8 ring[AHEAD];
 #pragma unroll
-    for (int s = 0; s < T::PSTEPS; ++s) {
+    for (int i = 0; i < AHEAD; ++i) ring[i] = operand(i);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[s][i] = (_Float16)sacc[s >> 1][8 * (s & 1) + i];
-      rs[s] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const half2 pp = {pf[s][2 * e], pf[s][2 * e + 1]};
-        rs[s] = __builtin_amdgcn_fdot2(pp, ones, rs[s], false);
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 a = ring[i % AHEAD];
+      if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
+      const int n = i >> 1;
+      if ((i & 1) == 0) {
+        const int st = n / T::DBLK, b = n % T::DBLK;
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st], oacc[b], 0, 0, 0);
+      } else {
+        const int kb = n / T::KSTEPS, st = n % T::KSTEPS;
+        const floatx16 c = st == 0 ? floatx16{} : sacc[kb];
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st], c, 0, 0, 0);
       }
     }
-    float rsum = rs[0];
-#pragma unroll
-    for (int s = 1; s < T::PSTEPS; ++s) rsum += rs[s];
-    l_run += rsum;
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- ping-pong schedule -------------------------------------------------------
   // Every wave runs the same sequence of barrier-separated local intervals.
-  // 2j is the matrix-core interval of iteration j: P_{j-1} -> fp16 and its row
-  // sum (vector work that issues between the MFMAs), U_{j-1}, T_j. 2j+1 is the
-  // vector interval: the producer work (write V^T_{j+1}, DMA K_{j+2}, load
-  // V_{j+2}) and the first half of C_j (mask, max, lazy rescale, exp2).
-  // Group 1 starts one interval late (an extra barrier up front, which group 0
-  // matches at the end), so in every interval one wave of each SIMD feeds the
-  // matrix core while the other runs the vector work.
+  // 2j is the matrix-core interval of iteration j: U_{j-1} and T_j. 2j+1 is
+  // the vector interval: the producer work (transpose V_{j+1} into V^T, DMA
+  // K_{j+2} and V_{j+3}) and C_j (mask, exp2, fp16 pack, row sum, and when
+  // needed the row max and lazy rescale). Group 1 starts one interval late
+  // (an extra barrier up front, which group 0 matches at the end), so in every
+  // interval one wave of each SIMD feeds the matrix core while the other runs
+  // the vector work. Global interval = local interval + group.
   //
-  // Rings (slot = tile % 3). K_j is read in global intervals 2j .. 2j+1 and
-  // V^T_j in 2j+2 .. 2j+3. In local interval 2j+1 a wave writes V^T_{j+1}
-  // (global 2j+1 or 2j+2) over V^T_{j-2}, last read in 2j-1, and DMAs K_{j+2}
-  // over K_{j-1}, last read in 2j-1. A wave waits for its K_{j+1} DMA at the end
-  // of local interval 2j and for its V^T writes at the end of each vector
-  // interval; the barrier after each wait precedes the first read. Loads past
-  // the sequence end return zeros into slots that are never read.
+  // Rings (slot = tile % 3).
+  // - K_t: DMA issued in local 2t-3, waited for at the end of local 2t-2
+  //   (mfma_sync), read in global 2t .. 2t+1; the next DMA into its slot is
+  //   issued in local 2t+3.
+  // - V_t (natural layout): DMA issued in local 2t-5, waited for at the end
+  //   of local 2t-3 (vector_sync), transposed in global 2t-1 .. 2t; the next
+  //   DMA into its slot is issued in local 2t+1.
+  // - V^T_t: written in global 2t-1 .. 2t, read in global 2t+2 .. 2t+3; the
+  //   next write to its slot is in global 2t+5.
+  // Each wait is followed by a barrier before any other wave reads. Loads
+  // past the sequence end return zeros into slots that are never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
-    // this wave's K_{j+1} DMA landed (its V_{j+1} register loads may not have)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
+    // this wave's K_{j+1} DMA landed (V_{j+3}, issued after it, may not have)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
   };
   auto vector_sync = [&]() __attribute__((always_inline)) {
-    // this wave's V^T writes are in LDS
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // this wave's V^T writes are in LDS and its V_{j+2} DMA landed
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
+  };
+  auto produce_issue = [&](int j) __attribute__((always_inline)) {
+    tr_read(j + 1);
+    fetch_k(j + 2, (j + 2) % T::SLOTS);
+    fetch_v(j + 3);
   };
   auto produce = [&](int j) __attribute__((always_inline)) {
-    store_vt((j + 1) % T::SLOTS);
-    fetch_k(j + 2, (j + 2) % T::SLOTS);
-    load_v(j + 2);
+    produce_issue(j);
+    tr_write(j + 1);
   };
 
   // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
   // compile time, so every LDS operand address is a lane register plus an
   // immediate.
   auto steady = [&](int j, auto u_tag) __attribute__((always_inline)) {
-    constexpr int U = decltype(u_tag)::value;
-    constexpr int PREV = (U + 2) % 3;
     // local interval 2j: matrix core
     __builtin_amdgcn_s_setprio(1);
-    softmax_pack();
-    pv(std::integral_constant<int, PREV>{});
-    qk(std::integral_constant<int, U>{});
-    // Operand reads run 6 MFMAs ahead of their MFMA, with one vector
-    // instruction of the P packing between consecutive MFMAs.
-    constexpr int AHEAD = 6;
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-    for (int i = 0; i < T::PSTEPS * T::DBLK + T::KSTEPS * T::KB - AHEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-    }
+    mfma_interval(u_tag);
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     // local interval 2j+1: vector ALU
-    produce(j);
-    softmax_exp(j);
+    produce_issue(j);
+    softmax_fast(j);
+    tr_write(j + 1);
     vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
@@ -414,21 +503,25 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   using U2 = std::integral_constant<int, 2>;
 
   fetch_k(0, 0);
+  fetch_v(0);
   fetch_k(1, 1);
-  load_v(0);
-  store_vt(0);
-  load_v(1);
-  // K_0, K_1 landed and V^T_0 written (V_1 may still be in flight)
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::V_KEYS_PER_WAVE) : "memory");
+  fetch_v(1);
+  fetch_v(2);
+  // K_0 and V_0 landed in every wave
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * T::LOADS_PER_WAVE) : "memory");
+  tr_read(0);
+  tr_write(0);
+  // V^T_0 written; K_1 and V_1 landed in every wave (V_2 may be in flight)
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
   if (group == 1) sync();
 
   // j = 0: T_0, then C_0
   if (n_wave > 0) qk(U0{});
   mfma_sync();
   produce(0);
-  if (n_wave > 0) softmax_exp(0);
+  if (n_wave > 0) softmax_max(0);
   vector_sync();
-  // 1 <= j < n_wave: P_{j-1}, U_{j-1}, T_j, then C_j
+  // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
   int j = 1;
   for (; j + 3 <= n_wave; j += 3) {
     steady(j, U1{});
@@ -446,10 +539,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
   // which the wave still produces its share of the workgroup's tiles
   for (; j <= n_kv; ++j) {
-    if (j == n_wave && j >= 1) {
-      softmax_pack();
-      pv((j - 1) % T::SLOTS);
-    }
+    if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
     mfma_sync();
     produce(j);
     vector_sync();
