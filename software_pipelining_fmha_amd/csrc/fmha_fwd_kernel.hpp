@@ -11,8 +11,8 @@
 // Register layouts (one 64-lane wave):
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_f16. A lane of the accumulator then holds 16 keys of
-//   one query column. So the row max and row sum are in-lane reductions
-//   plus one swap between the two 32-lane halves.
+//   one query column. So the row max is an in-lane reduction plus one swap
+//   between the two 32-lane halves.
 // * Key rows are written to LDS under a permutation that swaps bits 2 and 3
 //   of the row index within each 32-row block. With it, accumulator register
 //   i of lane-half h holds key 16*(i/8) + 8*h + i%8. Eight consecutive
@@ -24,6 +24,8 @@
 //   ds_read_b64_tr_b16 returns it column-wise.
 // * O^T accumulates with one query per lane column. The per-row rescale
 //   factor is therefore a per-lane scalar.
+// * Row sums of P run on the matrix core as well (one 16x16x32 MFMA per PV
+//   k-step), so the vector ALU only forms the weights.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,15 +38,13 @@ namespace fmha {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
 // Reference-max slack (base 2) before O and l are rescaled.
 constexpr float RESCALE_LOG2 = 8.0f;
-// Largest per-lane sum of one tile's weights accepted without a row max.
-// Every weight is then at most this bound, well inside the fp16 range.
-constexpr float WEIGHT_BOUND = 4096.0f;
 // MFMA slots by which an LDS operand read precedes its MFMA.
 constexpr int OPERAND_AHEAD = 4;
 
@@ -119,6 +119,15 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max(a, b, c) in one instruction. Scores are never NaN here (MFMA results or
+// -inf from masking), so no quieting of the inputs is needed, which fmaxf
+// would add in IEEE mode.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Key held by row p of an LDS K tile: bits 2 and 3 of p swapped (an involution).
 __device__ __forceinline__ int key_of_row(int p) {
   const int flip = ((p >> 2) ^ (p >> 3)) & 1;
@@ -188,7 +197,20 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
   float m_run = -INFINITY;  // reference max of scaled scores (base-2 domain)
-  float l_run = 0.f;        // this lane's share of the running sum
+  // Row sums of P on the matrix core: v_mfma_f32_16x16x32_f16 with a 0/1 A
+  // operand and P^T_j (as laid out for the 32x32x16 U MFMA) as B. Read as a
+  // 16x16x32 operand, lane l of that B holds keys 8*(l/32) .. +7 of query
+  // 16*((l/16)%2) + l%16. A row 0 selects the key groups of queries 0..15
+  // (lanes 0, 32), A row 4 those of queries 16..31 (lanes 20, 52). Register 0
+  // of lane q < 32 of the accumulator then holds the row sum of query q; every
+  // other element stays 0. The sum adds exactly the fp16 weights of U, in fp32.
+  floatx4 lacc = {0.f, 0.f, 0.f, 0.f};
+  half8 ones_a;
+  {
+    const _Float16 one = (lane == 0 || lane == 32 || lane == 20 || lane == 52) ? (_Float16)1.f : (_Float16)0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones_a[e] = one;
+  }
 
   const int n_kv_all = (N + T::BN - 1) / T::BN;
   const int n_kv = CAUSAL ? min(n_kv_all, (q0 + T::BM + T::BN - 1) / T::BN) : n_kv_all;
@@ -289,6 +311,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
 
   floatx16 sacc[T::KB];   // S_j^T (fp32)
   half8 pf[T::PSTEPS];    // P_j^T in fp16: B operand of PV_j
+  // Row sums of P_j for PV k-step st.
+  auto row_sum = [&](int st) __attribute__((always_inline)) {
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_a, pf[st], lacc, 0, 0, 0);
+  };
 
   // T stage for key tile j: S^T = K_j Q^T.
   auto qk = [&](auto slot) __attribute__((always_inline)) {
@@ -315,6 +341,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
         const half8 a = *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * s);
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[b], 0, 0, 0);
       }
+#pragma unroll
+    for (int s = 0; s < T::PSTEPS; ++s) row_sum(s);
   };
 
   const float c2 = p.scale_log2;
@@ -333,9 +361,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
         }
     }
   };
-  // P_j^T in fp16 (pf, the B operand of U_j) from p = 2^(s*c2 - m_run), and
-  // this lane's share of the row sum. The sum adds the fp16 weights that
-  // multiply V (v_fma_mix_f32 reads each half exactly), in fp32.
+  // P_j^T in fp16 (pf, the B operand of U_j): p = 2^(s*c2 - m_run).
   auto exp_pack = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < T::PSTEPS; ++st)
@@ -343,65 +369,52 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
       for (int i = 0; i < 8; ++i)
         pf[st][i] = (_Float16)__builtin_amdgcn_exp2f(
             __builtin_fmaf(sacc[st >> 1][8 * (st & 1) + i], c2, -m_run));
-    float part[T::PSTEPS];
-#pragma unroll
-    for (int st = 0; st < T::PSTEPS; ++st) {
-      const intx4 w = __builtin_bit_cast(intx4, pf[st]);
-      part[st] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // part += lo(w[e]) * 1 and part += hi(w[e]) * 1, fp16 inputs, fp32 math
-        asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(part[st]) : "v"(w[e]));
-        asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(part[st]) : "v"(w[e]));
-      }
-    }
-    return (part[0] + part[1]) + (part[2] + part[3]);
   };
-  // Row max of the masked scores and the lazy rescale of O and l.
-  auto max_rescale = [&]() __attribute__((always_inline)) {
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
+  // Row max of the masked scores (base-2 domain), as a shallow tree.
+  auto tile_max = [&]() __attribute__((always_inline)) {
+    // 32 scores: 11 + 4 + 2 + 1 max3, depth 4
+    float t[11];
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
+    for (int k = 0; k < 10; ++k) {
+      const int a = 3 * k;
+      t[k] = max3(sacc[a >> 4][a & 15], sacc[(a + 1) >> 4][(a + 1) & 15], sacc[(a + 2) >> 4][(a + 2) & 15]);
+    }
+    t[10] = max3(sacc[1][14], sacc[1][15], sacc[1][15]);
+    const float u0 = max3(t[0], t[1], t[2]), u1 = max3(t[3], t[4], t[5]);
+    const float u2 = max3(t[6], t[7], t[8]), u3 = max3(t[9], t[10], t[10]);
+    const float mx = max3(max3(u0, u1, u2), u3, u3);
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1])) * c2;
+  };
+  // C stage for key tile j. The weights are first formed against the current
+  // reference max; the row max, computed alongside, only decides whether the
+  // reference must move. It moves only when some row's max grows by more than
+  // 2^RESCALE_LOG2, so p <= 2^RESCALE_LOG2 always. O and l share the
+  // reference, so O / l is unchanged when it stays. When it moves, O and l
+  // are rescaled (they hold every earlier tile here: U_{j-1} and its row sum
+  // ran in the matrix-core interval before C_j) and the weights are formed
+  // again from the scores, which are still intact.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    exp_pack();
+    // the weights are formed here, before the branch, not inside it
 #pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    const float m_tile = max_halves(mx) * c2;
-    // The reference max moves only when some row's max grows by more than
-    // 2^RESCALE_LOG2. Until then p <= 2^RESCALE_LOG2; O and l share the same
-    // reference, so O / l is unchanged and the rescale of O is skipped. O and l
-    // already hold every earlier tile here (U_{j-1} ran before C_j).
+    for (int st = 0; st < T::PSTEPS; ++st) asm volatile("" : "+v"(pf[st]));
+    const float m_tile = tile_max();
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
+      lacc *= alpha;  // lane q < 32 holds query q, as alpha does
 #pragma unroll
       for (int b = 0; b < T::DBLK; ++b) oacc[b] *= alpha;
+      exp_pack();
     }
-  };
-  // C stage with the exact tile max (the first tile of a wave).
-  auto softmax_max = [&](int j) __attribute__((always_inline)) {
-    mask_tile(j);
-    max_rescale();
-    l_run += exp_pack();
-    asm volatile("" : "+v"(l_run));
-  };
-  // C stage for a later tile: weights against the current reference first.
-  // A lane's partial sum bounds each of its weights, so while every partial
-  // sum stays within WEIGHT_BOUND no row max is needed. Otherwise the scores,
-  // still intact, take the exact path.
-  auto softmax_fast = [&](int j) __attribute__((always_inline)) {
-    mask_tile(j);
-    float part = exp_pack();
-    if (__builtin_amdgcn_ballot_w64(!(part <= WEIGHT_BOUND)) != 0) {
-      max_rescale();
-      part = exp_pack();
-    }
-    l_run += part;
-    asm volatile("" : "+v"(l_run));
   };
   // Matrix-core interval of a steady iteration: U_{j-1} (V^T slot PREV) and
-  // T_j (K slot U), 2 * NPV MFMAs in a fixed order. Even slots are U MFMAs,
-  // odd slots T MFMAs, so consecutive MFMAs never share an accumulator. Each
+  // T_j (K slot U), 2 * NPV MFMAs in a fixed order, plus the row-sum MFMA
+  // after the last U MFMA of each k-step. Even slots are U MFMAs, odd slots
+  // T MFMAs, so consecutive MFMAs never share an accumulator. Each
   // LDS operand is read OPERAND_AHEAD slots before its MFMA; scheduling
   // barriers keep that order, so each MFMA waits only for its own operand.
   auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
@@ -434,6 +447,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
       if ((i & 1) == 0) {
         const int st = n / T::DBLK, b = n % T::DBLK;
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st], oacc[b], 0, 0, 0);
+        if (b == T::DBLK - 1) row_sum(st);
       } else {
         const int kb = n / T::KSTEPS, st = n % T::KSTEPS;
         const floatx16 c = st == 0 ? floatx16{} : sacc[kb];
@@ -447,8 +461,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // Every wave runs the same sequence of barrier-separated local intervals.
   // 2j is the matrix-core interval of iteration j: U_{j-1} and T_j. 2j+1 is
   // the vector interval: the producer work (transpose V_{j+1} into V^T, DMA
-  // K_{j+2} and V_{j+3}) and C_j (mask, exp2, fp16 pack, row sum, and when
-  // needed the row max and lazy rescale). Group 1 starts one interval late
+  // K_{j+2} and V_{j+3}) and C_j (mask, exp2, fp16 pack, row max, and when
+  // needed the lazy rescale). Group 1 starts one interval late
   // (an extra barrier up front, which group 0 matches at the end), so in every
   // interval one wave of each SIMD feeds the matrix core while the other runs
   // the vector work. Global interval = local interval + group.
@@ -494,7 +508,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     mfma_sync();
     // local interval 2j+1: vector ALU
     produce_issue(j);
-    softmax_fast(j);
+    softmax(j);
     tr_write(j + 1);
     vector_sync();
   };
@@ -519,7 +533,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   if (n_wave > 0) qk(U0{});
   mfma_sync();
   produce(0);
-  if (n_wave > 0) softmax_max(0);
+  if (n_wave > 0) softmax(0);
   vector_sync();
   // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
   int j = 1;
@@ -549,7 +563,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2 -------------------
-  const float l_tot = sum_halves(l_run);
+  // lanes q and q + 32 hold query q; the row sum sits in lane q (lane q + 32 has 0)
+  const float l_tot = sum_halves(lacc[0]);
   const float inv = 1.f / l_tot;
   if (qrow < N) {
     _Float16* orow = p.o + head + (size_t)qrow * D;
