@@ -26,6 +26,14 @@
 //   factor is therefore a per-lane scalar.
 // * Row sums of P run on the matrix core as well (one 16x16x32 MFMA per PV
 //   k-step), so the vector ALU only forms the weights.
+//
+// Exponent reference: softmax is the same for any per-row offset, and the
+// running max only keeps the weights in range. So after the first key tile
+// the C stage keeps that tile's row max as a fixed reference and forms no
+// row max at all. If a later score exceeds the reference by 16 (base 2), its
+// weight overflows fp16 and the row sum turns non-finite. The workgroup then
+// recomputes its tile with the running max and lazy rescale, so every
+// output is the exact-path output in that case.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -394,6 +402,13 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // are rescaled (they hold every earlier tile here: U_{j-1} and its row sum
   // ran in the matrix-core interval before C_j) and the weights are formed
   // again from the scores, which are still intact.
+  // Without the row max: the reference stays at tile 0's max. Weights stay
+  // finite while no score exceeds it by 16 (base 2); past that they overflow
+  // fp16, the row sum becomes inf, and the workgroup reruns the exact path.
+  auto softmax_fast = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    exp_pack();
+  };
   auto softmax = [&](int j) __attribute__((always_inline)) {
     mask_tile(j);
     exp_pack();
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
   // compile time, so every LDS operand address is a lane register plus an
   // immediate.
-  auto steady = [&](int j, auto u_tag) __attribute__((always_inline)) {
+  auto steady = [&](int j, auto u_tag, auto exact_tag) __attribute__((always_inline)) {
     // local interval 2j: matrix core
     __builtin_amdgcn_s_setprio(1);
     mfma_interval(u_tag);
@@ -508,7 +523,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
     mfma_sync();
     // local interval 2j+1: vector ALU
     produce_issue(j);
-    softmax(j);
+    if constexpr (decltype(exact_tag)::value) softmax(j);
+    else softmax_fast(j);
     tr_write(j + 1);
     vector_sync();
   };
@@ -516,51 +532,79 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   using U1 = std::integral_constant<int, 1>;
   using U2 = std::integral_constant<int, 2>;
 
-  fetch_k(0, 0);
-  fetch_v(0);
-  fetch_k(1, 1);
-  fetch_v(1);
-  fetch_v(2);
-  // K_0 and V_0 landed in every wave
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * T::LOADS_PER_WAVE) : "memory");
-  tr_read(0);
-  tr_write(0);
-  // V^T_0 written; K_1 and V_1 landed in every wave (V_2 may be in flight)
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
-  if (group == 1) sync();
+  // The whole K/V pipeline; the fast variant skips the row max after tile 0.
+  auto run_pipeline = [&](auto exact_tag) __attribute__((always_inline)) {
+    fetch_k(0, 0);
+    fetch_v(0);
+    fetch_k(1, 1);
+    fetch_v(1);
+    fetch_v(2);
+    // K_0 and V_0 landed in every wave
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * T::LOADS_PER_WAVE) : "memory");
+    tr_read(0);
+    tr_write(0);
+    // V^T_0 written; K_1 and V_1 landed in every wave (V_2 may be in flight)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
+    if (group == 1) sync();
 
-  // j = 0: T_0, then C_0
-  if (n_wave > 0) qk(U0{});
-  mfma_sync();
-  produce(0);
-  if (n_wave > 0) softmax(0);
-  vector_sync();
-  // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
-  int j = 1;
-  for (; j + 3 <= n_wave; j += 3) {
-    steady(j, U1{});
-    steady(j + 1, U2{});
-    steady(j + 2, U0{});
-  }
-  if (j < n_wave) {
-    steady(j, U1{});
-    ++j;
+    // j = 0: T_0, then C_0
+    if (n_wave > 0) qk(U0{});
+    mfma_sync();
+    produce(0);
+    if (n_wave > 0) softmax(0);
+    vector_sync();
+    // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
+    int j = 1;
+    for (; j + 3 <= n_wave; j += 3) {
+      steady(j, U1{}, exact_tag);
+      steady(j + 1, U2{}, exact_tag);
+      steady(j + 2, U0{}, exact_tag);
+    }
     if (j < n_wave) {
-      steady(j, U2{});
+      steady(j, U1{}, exact_tag);
       ++j;
+      if (j < n_wave) {
+        steady(j, U2{}, exact_tag);
+        ++j;
+      }
+    }
+    // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
+    // which the wave still produces its share of the workgroup's tiles
+    for (; j <= n_kv; ++j) {
+      if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
+      mfma_sync();
+      produce(j);
+      vector_sync();
+    }
+    if (group == 0) sync();
+    // no load may still be in flight when the workgroup exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  run_pipeline(std::false_type{});
+  {
+    // Any weight overflow shows as a non-finite row sum; the workgroup then
+    // reruns with the row max and lazy rescale (the rings are idle here).
+    const float l_fast = sum_halves(lacc[0]);
+    const bool bad = __builtin_amdgcn_ballot_w64(!(l_fast < INFINITY)) != 0;
+    // the flags sit in the staging ring, which trailing DMAs of other waves
+    // may still be writing until every wave has passed its vmcnt(0)
+    sync();
+    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)v_stage;
+    if (lane == 0) flags[wave] = bad ? 1 : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < T::WAVES; ++w) any |= flags[w];
+    any = __builtin_amdgcn_readfirstlane(any);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (any) {
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b) oacc[b] = floatx16{};
+      lacc = floatx4{};
+      m_run = -INFINITY;
+      run_pipeline(std::true_type{});
     }
   }
-  // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
-  // which the wave still produces its share of the workgroup's tiles
-  for (; j <= n_kv; ++j) {
-    if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
-    mfma_sync();
-    produce(j);
-    vector_sync();
-  }
-  if (group == 0) sync();
-  // no load may still be in flight when the workgroup exits
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2 -------------------
   // lanes q and q + 32 hold query q; the row sum sits in lane q (lane q + 32 has 0)

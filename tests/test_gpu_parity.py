@@ -117,6 +117,51 @@ def test_full_size_uniform_keys_every_row(N, causal, device):
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("d,causal", [(64, False), (128, False), (64, True), (128, True)])
+def test_late_scores_far_above_first_key_tile(d, causal, device):
+    """For one block of query rows, the best key past the first 64 scores
+    more than 2^28 above every key of the first 64. A weight formed against
+    the first tile's row max overflows fp16 there, so these rows take the
+    running-max path; the other rows of their workgroup are recomputed with
+    them. Every row is compared with the oracle."""
+    B, H, N = 1, 2, 700
+    print("late large scores d=%d causal=%d" % (d, causal), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=31 + d + causal)
+    q[:, 0, 300:340, 7] = 16
+    k[:, 0, 64:, 7] = 16
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
+    s = float(scale) * np.einsum("nd,md->nm", q[0, 0, 300:340].astype(np.float64),
+                                 k[0, 0].astype(np.float64))
+    gap = (s[:, 64:].max(axis=1) - s[:, :64].max(axis=1)) / math.log(2)
+    assert gap.min() > 17, "inputs do not reach the overflow case"
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    check_rows(o, lse, rows, o_ref.reshape(-1, d), lse_ref.reshape(-1), "late-large")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_late_scores_just_inside_fp16_weights(d, device):
+    """Keys past the first tile score 2^13 to 2^15 above the first tile's
+    max: the weights stay finite but reach thousands, with no rescale."""
+    B, H, N = 1, 1, 640
+    print("late scores inside fp16 d=%d" % d, flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=57 + d)
+    q = (q.astype(np.float32) * 0.05).astype(np.float16)
+    k = (k.astype(np.float32) * 0.05).astype(np.float16)
+    scale = np.float32(1 / math.sqrt(d))
+    target = 14.0 * math.log(2)  # natural-log gap
+    q[..., 3] = 8
+    k[:, :, 64:, 3] = np.float16(target / (8 * float(scale)))
+    o, lse = run(q, k, v, False, scale)
+    o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=False, scale=scale)
+    s = float(scale) * np.einsum("nd,md->nm", q[0, 0].astype(np.float64), k[0, 0].astype(np.float64))
+    gap = (s[:, 64:].max(axis=1) - s[:, :64].max(axis=1)) / math.log(2)
+    assert 12 < gap.min() and gap.max() < 15.5, (gap.min(), gap.max())
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    check_rows(o, lse, rows, o_ref.reshape(-1, d), lse_ref.reshape(-1), "late-inside")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_one_hot_scores_select_one_value_row(d, device):
     N = 300
