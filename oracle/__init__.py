@@ -1,4 +1,4 @@
-"""CPU oracle for the fused multi-head attention forward pass.
+"""CPU oracle for the fused multi-head attention forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench
 script's CPU-baseline leg may import this package. The HIP library and its
@@ -6,12 +6,15 @@ Python binding never import it, and it imports nothing from them.
 
 `fmha_oracle.c` holds the arithmetic: the plain fp64 definition
 softmax(scale * Q K^T) V, plus the natural-log logsumexp of each row, one
-query row at a time. The pages name the stages: QK^T, then softmax, then PV
-(Tawa, section III-D), and the load/mma/softmax/rescale tasks (PipeThreader,
-"core method"). This module only builds the C library and marshals arrays
-for it.
+query row at a time; and the gradients of sum(dO * O) with respect to Q, K
+and V, one row at a time, by the chain rule through that definition (the
+backward kernel Twill schedules in sections 6.3 and 6.4). The pages name the
+stages: QK^T, then softmax, then PV (Tawa, section III-D), and the
+load/mma/softmax/rescale tasks (PipeThreader, "core method"). This module
+only builds the C library and marshals arrays for it.
 
-Every function here is pinned by `tests/test_oracle.py`.
+Every function here is pinned by `tests/test_oracle.py` (forward) and
+`tests/test_oracle_bwd.py` (backward).
 """
 from __future__ import annotations
 
@@ -49,6 +52,13 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_fmha_bwd_rows.restype = ctypes.c_int
+        lib.oracle_fmha_bwd_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_half_to_double.restype = None
         lib.oracle_half_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int64]
@@ -107,3 +117,42 @@ def fmha_all(q, k, v, *, causal: bool, scale, threads: int | None = None):
     rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
     o, lse = fmha_rows(q, k, v, rows, causal=causal, scale=scale, threads=threads)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def fmha_bwd_rows(q, k, v, dout, qrows, krows, *, causal: bool, scale,
+                  threads: int | None = None):
+    """Gradients of sum(dout * O) for selected rows.
+
+    q, k, v, dout: float16 [B, H, N, d]. qrows, krows: int [n, 3] triples
+    (b, h, i). Returns (dq float64 [n_q, d], dk float64 [n_k, d],
+    dv float64 [n_k, d]). Each distinct head among krows costs one forward
+    pass over that head.
+    """
+    q, k, v, dout = _as_half(q), _as_half(k), _as_half(v), _as_half(dout)
+    if q.ndim != 4 or not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64).reshape(-1, 3)
+    krows = np.ascontiguousarray(krows, dtype=np.int64).reshape(-1, 3)
+    dq = np.empty((qrows.shape[0], d), dtype=np.float64)
+    dk = np.empty((krows.shape[0], d), dtype=np.float64)
+    dv = np.empty((krows.shape[0], d), dtype=np.float64)
+    st = _load().oracle_fmha_bwd_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, B, H, N, d,
+        int(bool(causal)), float(scale), qrows.ctypes.data, qrows.shape[0], dq.ctypes.data,
+        krows.ctypes.data, krows.shape[0], dk.ctypes.data, dv.ctypes.data,
+        int(threads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_fmha_bwd_rows failed with status %d" % st)
+    return dq, dk, dv
+
+
+def fmha_bwd_all(q, k, v, dout, *, causal: bool, scale, threads: int | None = None):
+    """Every row: returns (dq, dk, dv), each float64 [B, H, N, d]."""
+    B, H, N, d = q.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+    dq, dk, dv = fmha_bwd_rows(q, k, v, dout, rows, rows, causal=causal, scale=scale,
+                               threads=threads)
+    shape = (B, H, N, d)
+    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)

@@ -1,5 +1,5 @@
 /*
- * CPU oracle for the fused multi-head attention forward pass.
+ * CPU oracle for the fused multi-head attention forward and backward passes.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench
  * script's CPU-baseline leg may load or call this file. The HIP library
@@ -24,6 +24,22 @@
  * Inputs are IEEE binary16 bit patterns in the [B, H, N, d] layout. They are
  * widened exactly to binary64. scale arrives as a double; callers pass the
  * float32 scale the kernel receives, widened.
+ *
+ * Backward pass. Twill (OSDI'26), sections 6.3 and 6.4, schedules the
+ * attention backward kernel on Hopper and Blackwell but prints no formula.
+ * The gradients here are those of the scalar L = sum_{i,c} dO[i][c] * o_i[c]
+ * with respect to q, k and v, written straight from the forward definition
+ * above (chain rule through the softmax):
+ *
+ *   P_ij  = exp(s_ij - lse_i)                  (the softmax weight, j in J_i)
+ *   D_i   = sum_c dO[i][c] * o_i[c]
+ *   dP_ij = sum_c dO[i][c] * v[j][c]
+ *   dS_ij = P_ij * (dP_ij - D_i)
+ *   dq_i  = scale * sum_{j in J_i} dS_ij * k_j
+ *   dk_j  = scale * sum_{i : j in J_i} dS_ij * q_i
+ *   dv_j  = sum_{i : j in J_i} P_ij * dO_i
+ *
+ * lse_i and o_i are recomputed here from q, k, v, never taken from a caller.
  */
 #include <math.h>
 #include <pthread.h>
@@ -204,4 +220,288 @@ int oracle_fmha_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(tids);
     free(started);
     return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward pass                                                              */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    const uint16_t *q, *k, *v, *dout;
+    int64_t H, N, d;
+    int causal;
+    double scale;
+} head_args_t;
+
+/* Forward quantities of query row i of head `head` (element offset of the
+ * head): lse_i and D_i = dO_i . o_i. s and od are scratch of N and d
+ * doubles. */
+static void row_stats(const head_args_t *a, int64_t head, int64_t i, double *s, double *od,
+                      double *lse_out, double *D_out)
+{
+    const int64_t N = a->N, d = a->d;
+    const uint16_t *qi = a->q + head + i * d;
+    const uint16_t *doi = a->dout + head + i * d;
+    const int64_t nvis = a->causal ? i + 1 : N;
+
+    for (int64_t j = 0; j < nvis; ++j) {
+        const uint16_t *kj = a->k + head + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += g_half[qi[c]] * g_half[kj[c]];
+        s[j] = a->scale * dot;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j)
+        if (s[j] > m)
+            m = s[j];
+    double l = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+        od[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double e = exp(s[j] - m);
+        const uint16_t *vj = a->v + head + j * d;
+        l += e;
+        for (int64_t c = 0; c < d; ++c)
+            od[c] += e * g_half[vj[c]];
+    }
+    double D = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+        D += g_half[doi[c]] * (od[c] / l);
+    *lse_out = m + log(l);
+    *D_out = D;
+}
+
+/* dq_i of one query row, from the definition. s is scratch of N doubles. */
+static void dq_row(const head_args_t *a, int64_t head, int64_t i, double *s, double *od,
+                   double *dq)
+{
+    const int64_t d = a->d;
+    const int64_t nvis = a->causal ? i + 1 : a->N;
+    const uint16_t *doi = a->dout + head + i * d;
+    double lse, D;
+    row_stats(a, head, i, s, od, &lse, &D); /* also leaves s_ij in s */
+    for (int64_t c = 0; c < d; ++c)
+        dq[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const uint16_t *vj = a->v + head + j * d;
+        const uint16_t *kj = a->k + head + j * d;
+        const double P = exp(s[j] - lse);
+        double dP = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dP += g_half[doi[c]] * g_half[vj[c]];
+        const double dS = P * (dP - D);
+        for (int64_t c = 0; c < d; ++c)
+            dq[c] += dS * g_half[kj[c]];
+    }
+    for (int64_t c = 0; c < d; ++c)
+        dq[c] *= a->scale;
+}
+
+/* dk_j and dv_j of one key row. lse and D hold the row statistics of every
+ * query row of the head. */
+static void dkdv_row(const head_args_t *a, int64_t head, int64_t j, const double *lse,
+                     const double *D, double *dk, double *dv)
+{
+    const int64_t N = a->N, d = a->d;
+    const uint16_t *kj = a->k + head + j * d;
+    const uint16_t *vj = a->v + head + j * d;
+    for (int64_t c = 0; c < d; ++c)
+        dk[c] = dv[c] = 0.0;
+    for (int64_t i = a->causal ? j : 0; i < N; ++i) {
+        const uint16_t *qi = a->q + head + i * d;
+        const uint16_t *doi = a->dout + head + i * d;
+        double dot = 0.0, dP = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            dot += g_half[qi[c]] * g_half[kj[c]];
+            dP += g_half[doi[c]] * g_half[vj[c]];
+        }
+        const double P = exp(a->scale * dot - lse[i]);
+        const double dS = P * (dP - D[i]);
+        for (int64_t c = 0; c < d; ++c) {
+            dv[c] += P * g_half[doi[c]];
+            dk[c] += dS * g_half[qi[c]];
+        }
+    }
+    for (int64_t c = 0; c < d; ++c)
+        dk[c] *= a->scale;
+}
+
+typedef struct {
+    const head_args_t *a;
+    int kind;             /* 0: row stats of a head, 1: dq rows, 2: dk/dv rows */
+    int64_t head;         /* kind 0 */
+    double *lse, *D;      /* kind 0 output, kind 2 input */
+    const int64_t *rows;  /* kinds 1, 2: n x 3 triples */
+    const int64_t *heads; /* kind 2: head offset per row */
+    const double *lse_of, *D_of; /* kind 2: per-row pointers into cached stats */
+    double *out0, *out1;
+    int64_t begin, end;
+    int status;
+} bjob_t;
+
+static void *bwd_worker(void *arg)
+{
+    bjob_t *jb = (bjob_t *)arg;
+    const head_args_t *a = jb->a;
+    double *s = (double *)malloc(sizeof(double) * (size_t)a->N);
+    double *od = (double *)malloc(sizeof(double) * (size_t)a->d);
+    if (!s || !od) {
+        jb->status = 3;
+        free(s);
+        free(od);
+        return NULL;
+    }
+    for (int64_t r = jb->begin; r < jb->end; ++r) {
+        if (jb->kind == 0) {
+            row_stats(a, jb->head, r, s, od, &jb->lse[r], &jb->D[r]);
+        } else if (jb->kind == 1) {
+            const int64_t *t = jb->rows + 3 * r;
+            const int64_t head = (t[0] * a->H + t[1]) * a->N * a->d;
+            dq_row(a, head, t[2], s, od, jb->out0 + r * a->d);
+        } else {
+            const int64_t *t = jb->rows + 3 * r;
+            const int64_t head = (t[0] * a->H + t[1]) * a->N * a->d;
+            const int64_t hs = (t[0] * a->H + t[1]);
+            /* lse_of / D_of are indexed by the head's slot in the cache */
+            const int64_t slot = jb->heads[hs];
+            dkdv_row(a, head, t[2], jb->lse_of + slot * a->N, jb->D_of + slot * a->N,
+                     jb->out0 + r * a->d, jb->out1 + r * a->d);
+        }
+    }
+    free(s);
+    free(od);
+    return NULL;
+}
+
+/* Runs `proto` over [0, n) split across `threads` workers. */
+static int run_jobs(const bjob_t *proto, int64_t n, int threads)
+{
+    if (n == 0)
+        return 0;
+    if (threads > n)
+        threads = (int)n;
+    bjob_t *jobs = (bjob_t *)calloc((size_t)threads, sizeof(bjob_t));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    int *started = (int *)calloc((size_t)threads, sizeof(int));
+    if (!jobs || !tids || !started) {
+        free(jobs);
+        free(tids);
+        free(started);
+        return 3;
+    }
+    int status = 0;
+    for (int t = 0; t < threads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].begin = n * t / threads;
+        jobs[t].end = n * (t + 1) / threads;
+        if (threads > 1 && pthread_create(&tids[t], NULL, bwd_worker, &jobs[t]) == 0)
+            started[t] = 1;
+        else
+            bwd_worker(&jobs[t]);
+    }
+    for (int t = 0; t < threads; ++t) {
+        if (started[t])
+            pthread_join(tids[t], NULL);
+        if (jobs[t].status)
+            status = jobs[t].status;
+    }
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
+}
+
+static int rows_in_range(const int64_t *rows, int64_t n, int64_t B, int64_t H, int64_t N)
+{
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t *t = rows + 3 * r;
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= N)
+            return 0;
+    }
+    return 1;
+}
+
+/*
+ * Gradients of L = sum(dO * O) for selected rows.
+ *   q, k, v, dout : binary16 bit patterns, [B, H, N, d] contiguous
+ *   qrows, n_q    : (b, h, i) triples; dq receives n_q x d doubles
+ *   krows, n_k    : (b, h, j) triples; dk and dv receive n_k x d doubles each
+ *   threads       : worker threads (>= 1)
+ * dk/dv rows need lse_i and D_i of every query row of their head, so each
+ * distinct head among krows costs one full forward pass over that head.
+ * Returns 0 on success, 1 on a bad argument (nothing written), 3 if memory
+ * or a thread could not be had.
+ */
+int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *dout, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int causal, double scale, const int64_t *qrows, int64_t n_q,
+                         double *dq, const int64_t *krows, int64_t n_k, double *dk,
+                         double *dv, int threads)
+{
+    if (!q || !k || !v || !dout || B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_q < 0 ||
+        n_k < 0 || threads < 1 || (n_q > 0 && (!qrows || !dq)) ||
+        (n_k > 0 && (!krows || !dk || !dv)))
+        return 1;
+    if (!rows_in_range(qrows, n_q, B, H, N) || !rows_in_range(krows, n_k, B, H, N))
+        return 1;
+    pthread_once(&g_half_once, build_half_table);
+
+    head_args_t a = {q, k, v, dout, H, N, d, causal, scale};
+    bjob_t proto;
+    memset(&proto, 0, sizeof(proto));
+    proto.a = &a;
+
+    proto.kind = 1;
+    proto.rows = qrows;
+    proto.out0 = dq;
+    int st = run_jobs(&proto, n_q, threads);
+    if (st || n_k == 0)
+        return st;
+
+    /* row statistics of every head that a dk/dv row belongs to */
+    int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(B * H));
+    if (!slot)
+        return 3;
+    for (int64_t x = 0; x < B * H; ++x)
+        slot[x] = -1;
+    int64_t n_heads = 0;
+    for (int64_t r = 0; r < n_k; ++r) {
+        const int64_t hs = krows[3 * r] * H + krows[3 * r + 1];
+        if (slot[hs] < 0)
+            slot[hs] = n_heads++;
+    }
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(n_heads * N));
+    double *D = (double *)malloc(sizeof(double) * (size_t)(n_heads * N));
+    if (!lse || !D) {
+        free(slot);
+        free(lse);
+        free(D);
+        return 3;
+    }
+    for (int64_t hs = 0; hs < B * H && st == 0; ++hs) {
+        if (slot[hs] < 0)
+            continue;
+        bjob_t sp = proto;
+        sp.kind = 0;
+        sp.head = hs * N * d;
+        sp.lse = lse + slot[hs] * N;
+        sp.D = D + slot[hs] * N;
+        st = run_jobs(&sp, N, threads);
+    }
+    if (st == 0) {
+        bjob_t kp = proto;
+        kp.kind = 2;
+        kp.rows = krows;
+        kp.heads = slot;
+        kp.lse_of = lse;
+        kp.D_of = D;
+        kp.out0 = dk;
+        kp.out1 = dv;
+        st = run_jobs(&kp, n_k, threads);
+    }
+    free(slot);
+    free(lse);
+    free(D);
+    return st;
 }

@@ -34,6 +34,36 @@ MUTANTS = {
 }
 
 
+# Slips in the backward pass; each must fail a pin of test_oracle_bwd.py.
+BWD_MUTANTS = {
+    "bwd: dk scale dropped": ("        dk[c] *= a->scale;", "        dk[c] *= 1.0;"),
+    "bwd: dq scale dropped": ("        dq[c] *= a->scale;", "        dq[c] *= 1.0;"),
+    "bwd: D sign flipped in dq": ("const double dS = P * (dP - D);", "const double dS = P * (dP + D);"),
+    "bwd: D sign flipped in dk": ("P * (dP - D[i])", "P * (dP + D[i])"),
+    "bwd: dv weighted by dS": ("dv[c] += P * g_half[doi[c]];", "dv[c] += dS * g_half[doi[c]];"),
+    "bwd: dk built from keys": ("dk[c] += dS * g_half[qi[c]];", "dk[c] += dS * g_half[kj[c]];"),
+    "bwd: dP with keys": ("dP += g_half[doi[c]] * g_half[vj[c]];\n        const double dS",
+                          "dP += g_half[doi[c]] * g_half[kj[c]];\n        const double dS"),
+    "bwd: strict causal edge in dk/dv": ("a->causal ? j : 0", "a->causal ? j + 1 : 0"),
+    "bwd: D from unnormalised output": ("(od[c] / l)", "od[c]"),
+    "bwd: weights without lse": ("exp(a->scale * dot - lse[i])", "exp(a->scale * dot)"),
+    "bwd: query gradient from values": ("dq[c] += dS * g_half[kj[c]];", "dq[c] += dS * g_half[vj[c]];"),
+}
+
+
+def _bwd_pin_calls():
+    from tests import test_oracle_bwd as bp
+    return [
+        lambda: bp.test_matches_torch_autograd(False),
+        lambda: bp.test_matches_torch_autograd(True),
+        lambda: bp.test_key_gradients_sum_to_zero(True),
+        lambda: bp.test_value_gradients_sum_to_output_gradients(True),
+        lambda: bp.test_uniform_keys_give_zero_query_gradient(False),
+        bp.test_single_key_closed_form,
+        bp.test_last_causal_key_sees_only_last_query,
+    ]
+
+
 def _pin_calls():
     calls = [
         pins.test_half_decode_exhaustive_matches_numpy,
@@ -65,18 +95,25 @@ def _build_mutant(tmp_path, name, old, new):
     return str(so)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, tmp_path, monkeypatch):
-    old, new = MUTANTS[name]
-    so = _build_mutant(tmp_path, name, old, new)
+EXPORTS = ("oracle_fmha_rows", "oracle_fmha_bwd_rows", "oracle_half_to_double")
+
+
+def _swap_in(so, monkeypatch):
     real = oracle._load()
     lib = ctypes.CDLL(so)
-    for fn in ("oracle_fmha_rows", "oracle_half_to_double"):
+    for fn in EXPORTS:
         getattr(lib, fn).restype = getattr(real, fn).restype
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BWD_MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name] if name in MUTANTS else BWD_MUTANTS[name]
+    so = _build_mutant(tmp_path, name, old, new)
+    _swap_in(so, monkeypatch)
     failures = 0
-    for call in _pin_calls():
+    for call in (_pin_calls() if name in MUTANTS else _bwd_pin_calls()):
         try:
             call()
         except (AssertionError, RuntimeError, FloatingPointError):
@@ -87,11 +124,6 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
 def test_unmutated_copy_passes_every_pin(tmp_path, monkeypatch):
     """Control: the same build of the untouched source fails no pin."""
     so = _build_mutant(tmp_path, "identity", "exp(s[j] - m)", "exp(s[j] - m)")
-    real = oracle._load()
-    lib = ctypes.CDLL(so)
-    for fn in ("oracle_fmha_rows", "oracle_half_to_double"):
-        getattr(lib, fn).restype = getattr(real, fn).restype
-        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
-    monkeypatch.setattr(oracle, "_lib", lib)
-    for call in _pin_calls():
+    _swap_in(so, monkeypatch)
+    for call in _pin_calls() + _bwd_pin_calls():
         call()
