@@ -1,6 +1,7 @@
 """Benchmark of the fused attention forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--pass fwd|bwd]
 
 A step is one fmha_fwd launch over the whole batch. The default workload is
 FP16, B=4, H=32, N=16384, d=128, non-causal; the Twill (section 6.2, Fig. 7)
@@ -13,6 +14,13 @@ Prints one JSON line. It includes the MFMA roofline of the kernel (average
 launch time from HIP events on the launch stream) and, on rank 0, the CPU
 oracle timed on a bounded row sample. The oracle's rows also check the
 timed output.
+
+--pass bwd times one fmha_bwd call per step instead (its three kernels: the
+row dot products D, dK/dV, dQ) on the same workload plus a seeded output
+gradient, after one untimed forward pass that supplies O and lse. It counts
+the usual 2.5x the forward's FLOPs (five matrix products of 2*N^2*d per
+head), although the kernels execute seven (S and dP are formed again for
+dQ).
 """
 from __future__ import annotations
 
@@ -35,12 +43,21 @@ METRIC = "FMHA fwd TFLOPS (fp16, B4 H32 d128, N=16384) and % of MFMA peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 KERNEL_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_kernel.hpp",
                   "software_pipelining_fmha_amd/csrc/fmha_api.hip")
+BWD_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_bwd_kernel.hpp",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fmha_fwd_b4h32n16384d128.txt")
 
 
 def kernel_digest() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bwd_digest() -> str:
+    h = hashlib.sha256()
+    for rel in BWD_SOURCES + KERNEL_SOURCES[1:]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -105,6 +122,108 @@ def cpu_baseline(q, k, v, w, scale, o_gpu, lse_gpu, target_s: float):
         "pass": bool(err_o <= 2e-3 and err_l <= 1e-3)}
 
 
+BWD_U = 2.0 ** -11
+
+
+def bwd_cpu_baseline(q, k, v, do, w, scale, grads, target_s: float):
+    """Time the CPU oracle's backward on a bounded sample of one head of the
+    workload (dq rows, and dk/dv rows, whose head costs one forward pass),
+    and check those rows of the GPU gradients with the parity tests' bar."""
+    import oracle
+
+    threads = cpu_threads()
+    idx = inputs.WORKLOADS.index(w)
+    rng = np.random.default_rng(4343 + idx)
+    b, h = 0, int(rng.integers(w.H))
+    n = int(min(w.N, 2048))
+    qi = np.sort(rng.choice(w.N, size=n, replace=False))
+    kj = np.sort(rng.choice(w.N, size=n, replace=False))
+    qrows = np.array([(b, h, i) for i in qi], dtype=np.int64)
+    krows = np.array([(b, h, j) for j in kj], dtype=np.int64)
+    t0 = time.perf_counter()
+    ref = oracle.fmha_bwd_rows(q, k, v, do, qrows, krows, causal=w.causal, scale=scale,
+                               threads=threads, rss=True)
+    dt = time.perf_counter() - t0
+    worst = 0.0
+    for name, (got, rows, r, rs, ds, c) in {
+            "dq": (grads[0], qrows, ref[0], ref[3], ref[6], 3),
+            "dk": (grads[1], krows, ref[1], ref[4], ref[7], 21),
+            "dv": (grads[2], krows, ref[2], ref[5], 0.0, 0)}.items():
+        g = got[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+        tol = 8 * BWD_U * rs + 2 * BWD_U * np.abs(r) + c * BWD_U * ds + 2.0 ** -16
+        worst = max(worst, float((np.abs(g - r) / tol).max()))
+    # Algorithmic work attributed to the sample: each (query, key) pair carries
+    # 10 d FLOPs (five products); a dq row covers half of its row's pairs and a
+    # dk/dv row half of its column's.
+    vis_q = (qi + 1) if w.causal else np.full(n, w.N)
+    vis_k = (w.N - kj) if w.causal else np.full(n, w.N)
+    flops = 5.0 * w.d * float(vis_q.sum() + vis_k.sum())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+        "sample": "head (b=%d, h=%d) of %s: %d dq rows and %d dk/dv rows (the latter need one "
+                  "forward pass over the head); %.1f s wall" % (b, h, w.name, n, n, dt),
+    }, {"rows": 2 * n, "max_err_over_bar": worst, "pass": bool(worst <= 1.0)}
+
+
+def bench_bwd(args, w, idx, q, k, v, scale, tq, tk, tv, dev, stream):
+    import torch
+
+    from software_pipelining_fmha_amd import fmha
+
+    do = inputs.workload_dout(idx)
+    tdo = torch.from_numpy(do).to(dev)
+    o, lse = fmha.forward(tq, tk, tv, causal=w.causal, scale=float(scale), stream=stream)
+    dq, dk, dv = (torch.empty_like(tq) for _ in range(3))
+    ws = torch.empty((2 * w.B * w.H * w.N,), dtype=torch.float32, device=dev)
+
+    def step():
+        fmha.backward(tq, tk, tv, o, lse, tdo, causal=w.causal, scale=float(scale), dq=dq, dk=dk,
+                      dv=dv, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    avg_ms = float(np.mean(call_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.5 * w.flops
+    result = {
+        "metric": "FMHA bwd TFLOPS (fp16, %s) and %% of MFMA peak" % w.name,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "k_gain": w.k_gain, "layout": "BHNd",
+                   "flops_per_step": flops, "seed": inputs.SEED_BASE + idx,
+                   "dout_seed": inputs.SEED_BASE + idx + inputs.DOUT_SEED_OFFSET},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (avg_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "timed_unit": "one fmha_bwd call (3 kernels)",
+                     "call_ms_avg": round(avg_ms, 4), "call_ms_min": round(min(call_ms), 4),
+                     "kernel_digest": bwd_digest()},
+    }
+    if not args.no_cpu_baseline:
+        grads = [x.cpu().numpy() for x in (dq, dk, dv)]
+        cb, parity = bwd_cpu_baseline(q, k, v, do, w, scale, grads, args.cpu_seconds)
+        result["cpu_baseline"] = cb
+        result["parity"] = parity
+    print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        return 1
+    return 0
+
+
 def copy_calibration(mib: int, steps: int) -> int:
     """A plain copy kernel of known size: `steps` launches that each read and
     write mib MiB."""
@@ -132,6 +251,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward pass (default) or the backward pass")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many MiB "
                          "per step (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -160,6 +281,8 @@ def main(argv=None) -> int:
     o = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.which == "bwd":
+        return bench_bwd(args, w, idx, q, k, v, scale, tq, tk, tv, dev, stream)
 
     def step():
         fmha.forward(tq, tk, tv, causal=w.causal, scale=float(scale), out=o, lse=lse,

@@ -1,6 +1,6 @@
 /*
  * fmha.h - C ABI of the MI355X (gfx950) fused multi-head attention forward
- * pass.
+ * and backward passes.
  *
  * The operation. For every batch b, head h and query row i:
  *   S   = scale * Q K^T      (one row: s_j = scale * q_i . k_j)
@@ -20,6 +20,8 @@
  */
 #ifndef FMHA_H
 #define FMHA_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -67,6 +69,43 @@ extern "C" {
  */
 int fmha_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/*
+ * fmha_bwd - enqueue the attention backward pass on `stream`.
+ *
+ * The gradients of the scalar sum_{b,h,i,c} dout[b,h,i,c] * o[b,h,i,c] with
+ * respect to q, k and v, where o is the forward output above. Per head, with
+ * P_ij = exp(scale * q_i . k_j - lse_i) over the visible keys:
+ *   D_i  = dout_i . o_i
+ *   dS_ij = P_ij * (dout_i . v_j - D_i)
+ *   dq = scale * dS K,   dk = scale * dS^T Q,   dv = P^T dout.
+ * Twill (OSDI'26), sections 6.3 and 6.4, schedules this backward kernel on
+ * Hopper and Blackwell; the pages give no formula, so the one above is the
+ * chain rule through the forward definition.
+ *
+ * q, k, v    : the forward inputs, binary16 [B, H, N, d] as for fmha_fwd.
+ * o, lse     : the forward outputs for the same q, k, v, causal and scale
+ *              (o binary16 [B, H, N, d], lse float32 [B, H, N]).
+ * dout       : binary16 [B, H, N, d], the gradient of the loss with respect to o.
+ * dq, dk, dv : binary16 [B, H, N, d], written.
+ * ws         : float32 device workspace of fmha_bwd_workspace_bytes(B, H, N)
+ *              bytes, caller-owned. The call overwrites it; on completion its
+ *              first B*H*N values hold D_i = dout_i . o_i.
+ * B, H, N, d, causal, scale, stream: as for fmha_fwd.
+ *
+ * Ownership and errors follow fmha_fwd: all buffers are caller-owned device
+ * memory; dq, dk, dv and ws must not overlap the inputs or one another. It
+ * launches three kernels in order on `stream` and allocates nothing. The
+ * result is deterministic (no atomics). Limits as for fmha_fwd, and
+ * B*H*N < 2^30.
+ */
+int fmha_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv, float *ws,
+             int B, int H, int N, int d, int causal, float scale, void *stream);
+
+/* fmha_bwd_workspace_bytes - bytes of the ws argument of fmha_bwd
+ * (2 * B * H * N floats; 0 if any size is <= 0). */
+size_t fmha_bwd_workspace_bytes(int B, int H, int N);
 
 /* fmha_status_str - static, human-readable text for a status code. */
 const char *fmha_status_str(int status);

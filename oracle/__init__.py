@@ -58,7 +58,9 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_half_to_double.restype = None
         lib.oracle_half_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int64]
@@ -120,13 +122,17 @@ def fmha_all(q, k, v, *, causal: bool, scale, threads: int | None = None):
 
 
 def fmha_bwd_rows(q, k, v, dout, qrows, krows, *, causal: bool, scale,
-                  threads: int | None = None):
+                  threads: int | None = None, rss: bool = False):
     """Gradients of sum(dout * O) for selected rows.
 
     q, k, v, dout: float16 [B, H, N, d]. qrows, krows: int [n, 3] triples
     (b, h, i). Returns (dq float64 [n_q, d], dk float64 [n_k, d],
     dv float64 [n_k, d]). Each distinct head among krows costs one forward
-    pass over that head.
+    pass over that head. With rss=True it also returns tolerance scales:
+    (dq, dk, dv, rss_q, rss_k, rss_v, ds_q, ds_k), where rss_* is, per
+    element, the root-sum-square of the terms summed into it, and ds_q, ds_k
+    bound how dq and dk move per unit relative error in the entries of the
+    forward output O through D_i = dO_i . O_i (see fmha_oracle.c).
     """
     q, k, v, dout = _as_half(q), _as_half(k), _as_half(v), _as_half(dout)
     if q.ndim != 4 or not (q.shape == k.shape == v.shape == dout.shape):
@@ -137,22 +143,25 @@ def fmha_bwd_rows(q, k, v, dout, qrows, krows, *, causal: bool, scale,
     dq = np.empty((qrows.shape[0], d), dtype=np.float64)
     dk = np.empty((krows.shape[0], d), dtype=np.float64)
     dv = np.empty((krows.shape[0], d), dtype=np.float64)
+    r = [np.empty_like(x) for x in (dq, dk, dv, dq, dk)] if rss else [None] * 5
+    ptr = [x.ctypes.data if x is not None else None for x in r]
     st = _load().oracle_fmha_bwd_rows(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, B, H, N, d,
         int(bool(causal)), float(scale), qrows.ctypes.data, qrows.shape[0], dq.ctypes.data,
         krows.ctypes.data, krows.shape[0], dk.ctypes.data, dv.ctypes.data,
-        int(threads or default_threads()))
+        *ptr, int(threads or default_threads()))
     if st != 0:
         raise RuntimeError("oracle_fmha_bwd_rows failed with status %d" % st)
-    return dq, dk, dv
+    return (dq, dk, dv, *r) if rss else (dq, dk, dv)
 
 
-def fmha_bwd_all(q, k, v, dout, *, causal: bool, scale, threads: int | None = None):
-    """Every row: returns (dq, dk, dv), each float64 [B, H, N, d]."""
+def fmha_bwd_all(q, k, v, dout, *, causal: bool, scale, threads: int | None = None,
+                 rss: bool = False):
+    """Every row: returns (dq, dk, dv), each float64 [B, H, N, d] (and the
+    five tolerance-scale arrays after them if rss=True)."""
     B, H, N, d = q.shape
     b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
     rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
-    dq, dk, dv = fmha_bwd_rows(q, k, v, dout, rows, rows, causal=causal, scale=scale,
-                               threads=threads)
-    shape = (B, H, N, d)
-    return dq.reshape(shape), dk.reshape(shape), dv.reshape(shape)
+    out = fmha_bwd_rows(q, k, v, dout, rows, rows, causal=causal, scale=scale,
+                        threads=threads, rss=rss)
+    return tuple(x.reshape(B, H, N, d) for x in out)

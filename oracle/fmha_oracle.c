@@ -234,10 +234,12 @@ typedef struct {
 } head_args_t;
 
 /* Forward quantities of query row i of head `head` (element offset of the
- * head): lse_i and D_i = dO_i . o_i. s and od are scratch of N and d
- * doubles. */
+ * head): lse_i, D_i = dO_i . o_i and, if w_out is not NULL,
+ * w_i = sum_c |dO[i][c]| * sum_j P_ij |v[j][c]| (how strongly D_i reacts to
+ * relative errors in the entries of o_i; a tolerance scale for callers).
+ * s and od are scratch of N and 2 d doubles. */
 static void row_stats(const head_args_t *a, int64_t head, int64_t i, double *s, double *od,
-                      double *lse_out, double *D_out)
+                      double *lse_out, double *D_out, double *w_out)
 {
     const int64_t N = a->N, d = a->d;
     const uint16_t *qi = a->q + head + i * d;
@@ -256,33 +258,50 @@ static void row_stats(const head_args_t *a, int64_t head, int64_t i, double *s, 
         if (s[j] > m)
             m = s[j];
     double l = 0.0;
+    double *av = od + d; /* sum_j e_j |v_jc| */
     for (int64_t c = 0; c < d; ++c)
-        od[c] = 0.0;
+        od[c] = av[c] = 0.0;
     for (int64_t j = 0; j < nvis; ++j) {
         const double e = exp(s[j] - m);
         const uint16_t *vj = a->v + head + j * d;
         l += e;
-        for (int64_t c = 0; c < d; ++c)
+        for (int64_t c = 0; c < d; ++c) {
             od[c] += e * g_half[vj[c]];
+            av[c] += e * fabs(g_half[vj[c]]);
+        }
     }
-    double D = 0.0;
-    for (int64_t c = 0; c < d; ++c)
+    double D = 0.0, w = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
         D += g_half[doi[c]] * (od[c] / l);
+        w += fabs(g_half[doi[c]]) * (av[c] / l);
+    }
     *lse_out = m + log(l);
     *D_out = D;
+    if (w_out)
+        *w_out = w;
 }
 
-/* dq_i of one query row, from the definition. s is scratch of N doubles. */
+/* dq_i of one query row, from the definition. s is scratch of N doubles.
+ * If rss is not NULL it receives, per element, sqrt(sum_j (scale dS_ij k_jc)^2):
+ * the root-sum-square of the terms (a tolerance scale for callers). If dsens
+ * is not NULL it receives scale * w_i * sum_j P_ij |k_jc|, the bound on how
+ * dq_i moves per unit relative error in o_i through D_i. */
 static void dq_row(const head_args_t *a, int64_t head, int64_t i, double *s, double *od,
-                   double *dq)
+                   double *dq, double *rss, double *dsens)
 {
     const int64_t d = a->d;
     const int64_t nvis = a->causal ? i + 1 : a->N;
     const uint16_t *doi = a->dout + head + i * d;
-    double lse, D;
-    row_stats(a, head, i, s, od, &lse, &D); /* also leaves s_ij in s */
+    double lse, D, w;
+    row_stats(a, head, i, s, od, &lse, &D, &w); /* also leaves s_ij in s */
+    if (dsens)
+        for (int64_t c = 0; c < d; ++c)
+            dsens[c] = 0.0;
     for (int64_t c = 0; c < d; ++c)
         dq[c] = 0.0;
+    if (rss)
+        for (int64_t c = 0; c < d; ++c)
+            rss[c] = 0.0;
     for (int64_t j = 0; j < nvis; ++j) {
         const uint16_t *vj = a->v + head + j * d;
         const uint16_t *kj = a->k + head + j * d;
@@ -293,21 +312,43 @@ static void dq_row(const head_args_t *a, int64_t head, int64_t i, double *s, dou
         const double dS = P * (dP - D);
         for (int64_t c = 0; c < d; ++c)
             dq[c] += dS * g_half[kj[c]];
+        if (rss)
+            for (int64_t c = 0; c < d; ++c)
+                rss[c] += (dS * g_half[kj[c]]) * (dS * g_half[kj[c]]);
+        if (dsens)
+            for (int64_t c = 0; c < d; ++c)
+                dsens[c] += P * fabs(g_half[kj[c]]);
     }
     for (int64_t c = 0; c < d; ++c)
         dq[c] *= a->scale;
+    if (rss)
+        for (int64_t c = 0; c < d; ++c)
+            rss[c] = a->scale * sqrt(rss[c]);
+    if (dsens)
+        for (int64_t c = 0; c < d; ++c)
+            dsens[c] *= a->scale * w;
 }
 
-/* dk_j and dv_j of one key row. lse and D hold the row statistics of every
- * query row of the head. */
+/* dk_j and dv_j of one key row. lse, D and W hold the row statistics of
+ * every query row of the head. If rk / rv are not NULL they receive the
+ * root-sum-square of the terms of each element, as in dq_row; if dsk is not
+ * NULL it receives scale * sqrt(sum_i (P_ij w_i q_ic)^2), the root-sum-square
+ * of the per-query D sensitivities of dk_j. */
 static void dkdv_row(const head_args_t *a, int64_t head, int64_t j, const double *lse,
-                     const double *D, double *dk, double *dv)
+                     const double *D, const double *W, double *dk, double *dv, double *rk,
+                     double *rv, double *dsk)
 {
     const int64_t N = a->N, d = a->d;
     const uint16_t *kj = a->k + head + j * d;
     const uint16_t *vj = a->v + head + j * d;
     for (int64_t c = 0; c < d; ++c)
         dk[c] = dv[c] = 0.0;
+    if (rk)
+        for (int64_t c = 0; c < d; ++c)
+            rk[c] = rv[c] = 0.0;
+    if (dsk)
+        for (int64_t c = 0; c < d; ++c)
+            dsk[c] = 0.0;
     for (int64_t i = a->causal ? j : 0; i < N; ++i) {
         const uint16_t *qi = a->q + head + i * d;
         const uint16_t *doi = a->dout + head + i * d;
@@ -322,20 +363,38 @@ static void dkdv_row(const head_args_t *a, int64_t head, int64_t j, const double
             dv[c] += P * g_half[doi[c]];
             dk[c] += dS * g_half[qi[c]];
         }
+        if (rk)
+            for (int64_t c = 0; c < d; ++c) {
+                rv[c] += (P * g_half[doi[c]]) * (P * g_half[doi[c]]);
+                rk[c] += (dS * g_half[qi[c]]) * (dS * g_half[qi[c]]);
+            }
+        if (dsk)
+            for (int64_t c = 0; c < d; ++c)
+                dsk[c] += (P * W[i] * g_half[qi[c]]) * (P * W[i] * g_half[qi[c]]);
     }
     for (int64_t c = 0; c < d; ++c)
         dk[c] *= a->scale;
+    if (rk)
+        for (int64_t c = 0; c < d; ++c) {
+            rk[c] = a->scale * sqrt(rk[c]);
+            rv[c] = sqrt(rv[c]);
+        }
+    if (dsk)
+        for (int64_t c = 0; c < d; ++c)
+            dsk[c] = a->scale * sqrt(dsk[c]);
 }
 
 typedef struct {
     const head_args_t *a;
     int kind;             /* 0: row stats of a head, 1: dq rows, 2: dk/dv rows */
     int64_t head;         /* kind 0 */
-    double *lse, *D;      /* kind 0 output, kind 2 input */
+    double *lse, *D, *W;  /* kind 0 output, kind 2 input */
     const int64_t *rows;  /* kinds 1, 2: n x 3 triples */
     const int64_t *heads; /* kind 2: head offset per row */
-    const double *lse_of, *D_of; /* kind 2: per-row pointers into cached stats */
+    const double *lse_of, *D_of, *W_of; /* kind 2: cached stats of the heads */
     double *out0, *out1;
+    double *rss0, *rss1; /* optional root-sum-square outputs, NULL to skip */
+    double *ds0;         /* optional D-sensitivity output, NULL to skip */
     int64_t begin, end;
     int status;
 } bjob_t;
@@ -345,7 +404,7 @@ static void *bwd_worker(void *arg)
     bjob_t *jb = (bjob_t *)arg;
     const head_args_t *a = jb->a;
     double *s = (double *)malloc(sizeof(double) * (size_t)a->N);
-    double *od = (double *)malloc(sizeof(double) * (size_t)a->d);
+    double *od = (double *)malloc(sizeof(double) * (size_t)(2 * a->d));
     if (!s || !od) {
         jb->status = 3;
         free(s);
@@ -354,11 +413,12 @@ static void *bwd_worker(void *arg)
     }
     for (int64_t r = jb->begin; r < jb->end; ++r) {
         if (jb->kind == 0) {
-            row_stats(a, jb->head, r, s, od, &jb->lse[r], &jb->D[r]);
+            row_stats(a, jb->head, r, s, od, &jb->lse[r], &jb->D[r], &jb->W[r]);
         } else if (jb->kind == 1) {
             const int64_t *t = jb->rows + 3 * r;
             const int64_t head = (t[0] * a->H + t[1]) * a->N * a->d;
-            dq_row(a, head, t[2], s, od, jb->out0 + r * a->d);
+            dq_row(a, head, t[2], s, od, jb->out0 + r * a->d, jb->rss0 ? jb->rss0 + r * a->d : NULL,
+                   jb->ds0 ? jb->ds0 + r * a->d : NULL);
         } else {
             const int64_t *t = jb->rows + 3 * r;
             const int64_t head = (t[0] * a->H + t[1]) * a->N * a->d;
@@ -366,7 +426,9 @@ static void *bwd_worker(void *arg)
             /* lse_of / D_of are indexed by the head's slot in the cache */
             const int64_t slot = jb->heads[hs];
             dkdv_row(a, head, t[2], jb->lse_of + slot * a->N, jb->D_of + slot * a->N,
-                     jb->out0 + r * a->d, jb->out1 + r * a->d);
+                     jb->W_of + slot * a->N, jb->out0 + r * a->d, jb->out1 + r * a->d,
+                     jb->rss0 ? jb->rss0 + r * a->d : NULL, jb->rss1 ? jb->rss1 + r * a->d : NULL,
+                     jb->ds0 ? jb->ds0 + r * a->d : NULL);
         }
     }
     free(s);
@@ -427,6 +489,11 @@ static int rows_in_range(const int64_t *rows, int64_t n, int64_t B, int64_t H, i
  *   q, k, v, dout : binary16 bit patterns, [B, H, N, d] contiguous
  *   qrows, n_q    : (b, h, i) triples; dq receives n_q x d doubles
  *   krows, n_k    : (b, h, j) triples; dk and dv receive n_k x d doubles each
+ *   rss_q, rss_k, rss_v : NULL, or like dq, dk, dv: per element the
+ *                   root-sum-square of the terms summed into it (tolerance
+ *                   scale for a comparison with rounded arithmetic)
+ *   ds_q, ds_k    : NULL, or like dq and dk: the D sensitivities described
+ *                   at dq_row and dkdv_row (dv does not depend on D)
  *   threads       : worker threads (>= 1)
  * dk/dv rows need lse_i and D_i of every query row of their head, so each
  * distinct head among krows costs one full forward pass over that head.
@@ -437,7 +504,8 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          const uint16_t *dout, int64_t B, int64_t H, int64_t N, int64_t d,
                          int causal, double scale, const int64_t *qrows, int64_t n_q,
                          double *dq, const int64_t *krows, int64_t n_k, double *dk,
-                         double *dv, int threads)
+                         double *dv, double *rss_q, double *rss_k, double *rss_v,
+                         double *ds_q, double *ds_k, int threads)
 {
     if (!q || !k || !v || !dout || B <= 0 || H <= 0 || N <= 0 || d <= 0 || n_q < 0 ||
         n_k < 0 || threads < 1 || (n_q > 0 && (!qrows || !dq)) ||
@@ -452,9 +520,13 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     memset(&proto, 0, sizeof(proto));
     proto.a = &a;
 
+    if ((rss_k == NULL) != (rss_v == NULL))
+        return 1;
     proto.kind = 1;
     proto.rows = qrows;
     proto.out0 = dq;
+    proto.rss0 = rss_q;
+    proto.ds0 = ds_q;
     int st = run_jobs(&proto, n_q, threads);
     if (st || n_k == 0)
         return st;
@@ -473,10 +545,12 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     }
     double *lse = (double *)malloc(sizeof(double) * (size_t)(n_heads * N));
     double *D = (double *)malloc(sizeof(double) * (size_t)(n_heads * N));
-    if (!lse || !D) {
+    double *W = (double *)malloc(sizeof(double) * (size_t)(n_heads * N));
+    if (!lse || !D || !W) {
         free(slot);
         free(lse);
         free(D);
+        free(W);
         return 3;
     }
     for (int64_t hs = 0; hs < B * H && st == 0; ++hs) {
@@ -487,6 +561,7 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
         sp.head = hs * N * d;
         sp.lse = lse + slot[hs] * N;
         sp.D = D + slot[hs] * N;
+        sp.W = W + slot[hs] * N;
         st = run_jobs(&sp, N, threads);
     }
     if (st == 0) {
@@ -496,12 +571,17 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
         kp.heads = slot;
         kp.lse_of = lse;
         kp.D_of = D;
+        kp.W_of = W;
         kp.out0 = dk;
         kp.out1 = dv;
+        kp.rss0 = rss_k;
+        kp.rss1 = rss_v;
+        kp.ds0 = ds_k;
         st = run_jobs(&kp, n_k, threads);
     }
     free(slot);
     free(lse);
     free(D);
+    free(W);
     return st;
 }

@@ -1,12 +1,13 @@
-// C ABI of the attention forward pass: argument checks, variant choice, and
-// the launch on the caller's stream. The operation and the error contract
-// are stated in include/fmha.h.
+// C ABI of the attention forward and backward passes: argument checks,
+// variant choice, and the launches on the caller's stream. The operations and
+// the error contract are stated in include/fmha.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "fmha.h"
+#include "fmha_bwd_kernel.hpp"
 #include "fmha_fwd_kernel.hpp"
 
 namespace {
@@ -83,6 +84,92 @@ extern "C" int fmha_fwd(const void* q, const void* k, const void* v, void* o, fl
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 64) return causal ? launch<64, true>(prm, s) : launch<64, false>(prm, s);
   return causal ? launch<128, true>(prm, s) : launch<128, false>(prm, s);
+}
+
+namespace {
+
+template <int D, bool CAUSAL>
+int launch_bwd(const fmha::BwdParams& prm, hipStream_t stream) {
+  using T = fmha::BwdTile<D>;
+  void* args[] = {const_cast<fmha::BwdParams*>(&prm)};
+  constexpr int rows_per_block = 256 / (D / 8);
+  const int delta_grid = (prm.rows + rows_per_block - 1) / rows_per_block;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_delta_kernel<D>),
+                                 dim3(delta_grid), dim3(256), args, 0, stream);
+  if (e != hipSuccess) return FMHA_ERR_HIP;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_dkdv_kernel<D, CAUSAL>),
+                      dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+  if (e != hipSuccess) return FMHA_ERR_HIP;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_dq_kernel<D, CAUSAL>),
+                      dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" size_t fmha_bwd_workspace_bytes(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return static_cast<size_t>(2) * B * H * N * sizeof(float);
+}
+
+extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H,
+                        int N, int d, int causal, float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || N == 0) return FMHA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws)
+    return FMHA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f)) return FMHA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FMHA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(ws, 4))
+    return FMHA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(N) + 256) * d * 2 >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+  const int64_t rows = static_cast<int64_t>(B) * H * N;
+  if (rows >= (int64_t(1) << 30)) return FMHA_ERR_UNSUPPORTED;
+  const int bt = fmha::BwdTile<128>::BT;
+  const int64_t n_t = (N + bt - 1) / bt;
+  const int64_t grid = static_cast<int64_t>(B) * H * n_t;
+  if (grid >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+
+  const uint64_t tb = static_cast<uint64_t>(rows) * d * 2;
+  const uint64_t lb = static_cast<uint64_t>(rows) * 4;
+  const void* ins[] = {q, k, v, o, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* out : outs) {
+    for (const void* in : ins)
+      if (overlap(out, tb, in, tb)) return FMHA_ERR_INVALID_ARGUMENT;
+    if (overlap(out, tb, lse, lb) || overlap(out, tb, ws, 2 * lb)) return FMHA_ERR_INVALID_ARGUMENT;
+    for (void* other : outs)
+      if (other != out && overlap(out, tb, other, tb)) return FMHA_ERR_INVALID_ARGUMENT;
+  }
+  for (const void* in : ins)
+    if (overlap(ws, 2 * lb, in, tb)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (overlap(ws, 2 * lb, lse, lb)) return FMHA_ERR_INVALID_ARGUMENT;
+
+  fmha::BwdParams prm;
+  prm.q = static_cast<const _Float16*>(q);
+  prm.k = static_cast<const _Float16*>(k);
+  prm.v = static_cast<const _Float16*>(v);
+  prm.o = static_cast<const _Float16*>(o);
+  prm.dout = static_cast<const _Float16*>(dout);
+  prm.lse = lse;
+  prm.dq = static_cast<_Float16*>(dq);
+  prm.dk = static_cast<_Float16*>(dk);
+  prm.dv = static_cast<_Float16*>(dv);
+  prm.ws = ws;
+  prm.N = N;
+  prm.rows = static_cast<int>(rows);
+  prm.n_t = static_cast<int>(n_t);
+  prm.total_wg = static_cast<int>(grid);
+  prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  prm.scale = scale;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 64) return causal ? launch_bwd<64, true>(prm, s) : launch_bwd<64, false>(prm, s);
+  return causal ? launch_bwd<128, true>(prm, s) : launch_bwd<128, false>(prm, s);
 }
 
 extern "C" const char* fmha_status_str(int status) {

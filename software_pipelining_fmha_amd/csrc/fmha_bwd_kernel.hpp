@@ -1,0 +1,475 @@
+// Backward pass of fused multi-head attention for gfx950 (MI355X, CDNA4).
+//
+// Given Q, K, V, the forward output O, its gradient dO and the forward
+// logsumexp, the gradients of sum(dO * O) are, per head,
+//   P_ij  = exp(scale * q_i . k_j - lse_i)      (recomputed, never stored)
+//   D_i   = dO_i . O_i
+//   dS_ij = P_ij * (dO_i . v_j - D_i)
+//   dQ    = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO.
+// Twill (OSDI'26), sections 6.3 and 6.4, schedules this kernel on Hopper and
+// Blackwell: on Hopper it is register-bound and gets no cross-iteration
+// pipelining, and FlashAttention 3 uses 80 x 128 tiles there.
+//
+// Three kernels, each one workgroup per (batch, head, 128-row tile):
+// 1. fmha_bwd_delta_kernel: D_i and -lse_i * log2(e) into the workspace
+//    (HBM-bound: reads O and dO once).
+// 2. fmha_bwd_dkdv_kernel: a workgroup owns 128 keys (32 per wave) and
+//    streams every query tile that sees them: S = Q K^T and dP = dO V^T
+//    (fp16 MFMA, fp32 accumulate), P and dS on the vector ALU, then
+//    dV^T += dO^T P and dK^T += Q^T dS on the matrix core.
+// 3. fmha_bwd_dq_kernel: a workgroup owns 128 queries and streams every key
+//    tile they see: S^T = K Q^T, dP^T = V dO^T, then dQ^T += K^T dS^T.
+// dQ is recomputed in its own pass rather than accumulated with atomics, so
+// no workspace beyond D and lse is needed and results are deterministic; the
+// price is S and dP computed twice (7 matrix products instead of 5).
+//
+// Streamed tiles go HBM -> registers -> LDS (the load of step t+1 is in
+// flight during the compute of step t) into a two-slot ring, as [row][d]
+// with 16-byte chunk c of row r at chunk c ^ swz(r). One layout serves both
+// reads: MFMA A operands of whole rows (ds_read_b128) and transposed A
+// operands (ds_read_b64_tr_b16, 8 rows of one d column), both free of LDS
+// bank conflicts.
+#pragma once
+
+#include "fmha_fwd_kernel.hpp"
+
+namespace fmha {
+
+struct BwdParams {
+  const _Float16* q;
+  const _Float16* k;
+  const _Float16* v;
+  const _Float16* o;
+  const _Float16* dout;
+  const float* lse;
+  _Float16* dq;
+  _Float16* dk;
+  _Float16* dv;
+  float* ws;         // [2][rows]: D_i, then -lse_i * log2(e)
+  int N;             // sequence length
+  int rows;          // B * H * N
+  int n_t;           // 128-row tiles per head
+  int total_wg;      // B * H * n_t
+  float scale_log2;  // scale * log2(e)
+  float scale;
+};
+
+template <int D>
+struct BwdTile {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int RW = 32;             // rows (keys or queries) a wave owns
+  static constexpr int BT = WAVES * RW;     // rows a workgroup owns
+  static constexpr int BS = 32;             // rows streamed per step
+  static constexpr int KSTEPS = D / 16;     // MFMA k-steps over d
+  static constexpr int DBLK = D / 32;       // 32-row blocks of d
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BS * D * 2;
+  static constexpr int CPL = TILE_BYTES / 16 / THREADS;  // chunks per lane per tile
+  static constexpr int STAT_BYTES = 2 * BS * 4;
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + STAT_BYTES;
+  static constexpr int LDS_BYTES = 2 * SLOT_BYTES;
+  static_assert(CPL >= 1 && CPL * 16 * THREADS == TILE_BYTES, "staging covers a tile");
+};
+
+// Chunk swizzle of the streamed tiles. For D = 128 (256-byte rows) it is a
+// bijection on r mod 16 whose top two bits are r mod 4; for D = 64 (128-byte
+// rows) a bijection on (r / 2) mod 8 whose top bit is (r / 2) mod 2. Either
+// way 16 consecutive rows read at one chunk, and 4 consecutive rows read at 4
+// consecutive chunks, hit distinct banks.
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int bwd_off(int row, int col) {  // byte offset of element (row, col)
+  return row * D * 2 + 16 * ((col >> 3) ^ bwd_swz<D>(row)) + 2 * (col & 7);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = dO_i . O_i and -lse_i * log2(e)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fmha_bwd_delta_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;         // threads per row, 8 elements each
+  constexpr int RPB = 256 / TPR;     // rows per block
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < p.rows) {
+    const half8 a = *reinterpret_cast<const half8*>(p.dout + (size_t)row * D + 8 * c);
+    const half8 b = *reinterpret_cast<const half8*>(p.o + (size_t)row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+  if (row < p.rows && c == 0) {
+    p.ws[row] = acc;
+    p.ws[p.rows + row] = -p.lse[row] * 1.4426950408889634f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the two streaming kernels
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stream {
+  using T = BwdTile<D>;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) half8 lds_half8;
+  typedef __attribute__((address_space(3))) intx4 lds_intx4;
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
+
+  // Staging of one step: two [BS][D] fp16 tiles (rows r0 .. r0+BS-1 of a and
+  // b) and BS values of each of two per-row statistics.
+  intx4 ra[T::CPL], rb[T::CPL];
+  float rs;
+  int g_off[T::CPL], l_off[T::CPL];
+
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int i = 0; i < T::CPL; ++i) {
+      const int x = tid + T::THREADS * i;
+      const int row = x / T::CPR, c = x % T::CPR;
+      g_off[i] = (row * D + 8 * c) * 2;
+      l_off[i] = row * D * 2 + 16 * (c ^ bwd_swz<D>(row));
+    }
+  }
+  template <bool STATS>
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b,
+                                       __amdgpu_buffer_rsrc_t s0, __amdgpu_buffer_rsrc_t s1,
+                                       int r0, int tid) {
+#pragma unroll
+    for (int i = 0; i < T::CPL; ++i) {
+      ra[i] = load16(a, r0 * D * 2 + g_off[i]);
+      rb[i] = load16(b, r0 * D * 2 + g_off[i]);
+    }
+    if (STATS && tid < 2 * T::BS)
+      rs = tid < T::BS ? load_f32(s0, (r0 + tid) * 4) : load_f32(s1, (r0 + tid - T::BS) * 4);
+  }
+  template <bool STATS>
+  __device__ __forceinline__ void store(lds_char* slot, int tid) {
+#pragma unroll
+    for (int i = 0; i < T::CPL; ++i) {
+      *(lds_intx4*)(slot + l_off[i]) = ra[i];
+      *(lds_intx4*)(slot + T::TILE_BYTES + l_off[i]) = rb[i];
+    }
+    if (STATS && tid < 2 * T::BS)
+      *(__attribute__((address_space(3))) float*)(slot + 2 * T::TILE_BYTES + 4 * tid) = rs;
+  }
+};
+
+// Transposed A operand (8 rows of one d column per lane) from two
+// ds_read_b64_tr_b16 reads.
+__device__ __forceinline__ half8 tr_pair(const __attribute__((address_space(3))) char* base, int off0,
+                                         int off1) {
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + off0));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + off1));
+  const half4 a = __builtin_bit_cast(half4, lo), b = __builtin_bit_cast(half4, hi);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-lane byte offsets into a streamed [BS][D] tile.
+// nat[s]: A operand of row key_of_row(l32) (MFMA row l32), d = 16 s + 8 hh .. +7.
+// tr[b][rd]: source of ds_read_b64_tr_b16 for the transposed A operand of
+//   d block b, k-step 0, rows 8 hh + 4 rd .. +3 (k-step 1 adds 16 rows). A
+//   source lane s of 16-lane group g reads 4 d values starting at column
+//   32 b + 16 (g % 2) + 4 sigma(s % 4) of row 8 hh + 4 rd + s / 4, with sigma
+//   swapping 1 and 2; result lane i then holds d column
+//   32 b + key_of_row(lane % 32), so the accumulator rows come out in
+//   natural d order (the same bit-2/3 trick as the row operands).
+template <int D>
+struct Offsets {
+  using T = BwdTile<D>;
+  int nat[T::KSTEPS];
+  int tr[T::DBLK][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int row = key_of_row(l32);
+#pragma unroll
+    for (int s = 0; s < T::KSTEPS; ++s) nat[s] = bwd_off<D>(row, 16 * s + 8 * hh);
+    const int s16 = lane & 15, g = lane >> 4;
+    const int sig = ((s16 & 1) << 1) | ((s16 >> 1) & 1);
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+        tr[b][rd] = bwd_off<D>(8 * hh + 4 * rd + (s16 >> 2), 32 * b + 16 * (g & 1) + 4 * sig);
+  }
+};
+
+// XCD-aware tile id: consecutive ids (the tiles of one head) run on one XCD.
+__device__ __forceinline__ int bwd_tile_id(int G) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int per = G >> 3, rem = G & 7;
+  return xcd * per + min(xcd, rem) + (bid >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK and dV: a workgroup owns 128 keys and streams the query tiles.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  using S = Stream<D>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
+  typename S::lds_char* const smem = (typename S::lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int t = bwd_tile_id(p.total_wg);
+  const int bh = t / p.n_t;
+  const int kt = t - bh * p.n_t;  // causal: low key tiles see the most queries, so go first
+  const int N = p.N;
+  const int k0 = kt * T::BT;
+  const int kw0 = k0 + wave * T::RW;
+  const int key = kw0 + l32;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.ws + (size_t)bh * N, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.ws + p.rows + (size_t)bh * N, (uint32_t)N * 4u);
+
+  // K and V rows of this wave's keys: the B operands of S = Q K^T and
+  // dP = dO V^T (lane column = key, lane half hh holds d = 16 s + 8 hh ..).
+  half8 kf[T::KSTEPS], vf[T::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s) {
+    kf[s] = __builtin_bit_cast(half8, load16(rk, (key * D + 16 * s + 8 * hh) * 2));
+    vf[s] = __builtin_bit_cast(half8, load16(rv, (key * D + 16 * s + 8 * hh) * 2));
+  }
+  floatx16 dkt[T::DBLK], dvt[T::DBLK];  // dK^T, dV^T: lane = key, rows = d
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dkt[b][i] = dvt[b][i] = 0.f;
+
+  S st;
+  st.init(tid);
+  Offsets<D> off;
+  off.init(lane);
+  const float c2 = p.scale_log2;
+
+  const int q_begin = CAUSAL ? k0 : 0;
+  const int n_steps = (N - q_begin + T::BS - 1) / T::BS;
+  st.template load<true>(rq, rdo, rD, rL, q_begin, tid);
+  st.template store<true>(smem, tid);
+
+  for (int step = 0; step < n_steps; ++step) {
+    __syncthreads();
+    const int q_s = q_begin + step * T::BS;
+    if (step + 1 < n_steps) st.template load<true>(rq, rdo, rD, rL, q_s + T::BS, tid);
+    const typename S::lds_char* sq = smem + (step & 1) * T::SLOT_BYTES;
+    const typename S::lds_char* sdo = sq + T::TILE_BYTES;
+    const typename S::lds_char* sstat = sq + 2 * T::TILE_BYTES;
+
+    // a causal step entirely before this wave's first key contributes nothing
+    if (!CAUSAL || q_s + T::BS - 1 >= kw0) {
+      // S = Q K^T and dP = dO V^T: lane = key, register i = query
+      // q_s + 16 (i / 8) + 8 hh + i % 8.
+      floatx16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < T::KSTEPS; ++k)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sq + off.nat[k]),
+                                                   kf[k], s, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < T::KSTEPS; ++k)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sdo + off.nat[k]),
+                                                    vf[k], dp, 0, 0, 0);
+      floatx4 dv4[4], nl4[4];  // D and -lse*log2(e) of the 16 queries
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+        dv4[g] = *(const typename S::lds_floatx4*)(sstat + 4 * r);
+        nl4[g] = *(const typename S::lds_floatx4*)(sstat + 4 * (T::BS + r));
+      }
+      // mask: causal diagonal, ragged queries or keys
+      const bool edge = (CAUSAL && q_s < kw0 + T::RW - 1) || q_s + T::BS > N || kw0 + T::RW > N;
+      half8 pf[2], dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nl4[i >> 2][i & 3]));
+        if (edge) {
+          const int q = q_s + 16 * (i >> 3) + 8 * hh + (i & 7);
+          if ((CAUSAL && q < key) || q >= N || key >= N) pv = 0.f;
+        }
+        pf[i >> 3][i & 7] = (_Float16)pv;
+        dsf[i >> 3][i & 7] = (_Float16)(pv * (dp[i] - dv4[i >> 2][i & 3]));
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (k = queries, two k-steps)
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const half8 a = tr_pair(sdo, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
+          dvt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], dvt[b], 0, 0, 0);
+        }
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const half8 a = tr_pair(sq, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
+          dkt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsf[ks], dkt[b], 0, 0, 0);
+        }
+    }
+    if (step + 1 < n_steps) st.template store<true>(smem + ((step + 1) & 1) * T::SLOT_BYTES, tid);
+  }
+
+  // epilogue: register i of block b holds d = 32 b + 16 (i / 8) + 8 hh + i % 8
+  if (key < N) {
+    _Float16* dkr = p.dk + head + (size_t)key * D;
+    _Float16* dvr = p.dv + head + (size_t)key * D;
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        half8 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wk[e] = (_Float16)(dkt[b][8 * g + e] * p.scale);
+          wv[e] = (_Float16)dvt[b][8 * g + e];
+        }
+        *reinterpret_cast<half8*>(dkr + 32 * b + 16 * g + 8 * hh) = wk;
+        *reinterpret_cast<half8*>(dvr + 32 * b + 16 * g + 8 * hh) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: a workgroup owns 128 queries and streams the key tiles.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(BwdTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdParams p) {
+  using T = BwdTile<D>;
+  using S = Stream<D>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
+  typename S::lds_char* const smem = (typename S::lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int t = bwd_tile_id(p.total_wg);
+  const int bh = t / p.n_t;
+  int qt = t - bh * p.n_t;
+  if (CAUSAL) qt = p.n_t - 1 - qt;  // heaviest query tiles first
+  const int N = p.N;
+  const int q0 = qt * T::BT;
+  const int qw0 = q0 + wave * T::RW;
+  const int qrow = qw0 + l32;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.ws + (size_t)bh * N, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.ws + p.rows + (size_t)bh * N, (uint32_t)N * 4u);
+
+  // Q and dO rows of this wave's queries: B operands of S^T = K Q^T and
+  // dP^T = V dO^T. Per-query statistics are per-lane scalars here.
+  half8 qf[T::KSTEPS], dof[T::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s) {
+    qf[s] = __builtin_bit_cast(half8, load16(rq, (qrow * D + 16 * s + 8 * hh) * 2));
+    dof[s] = __builtin_bit_cast(half8, load16(rdo, (qrow * D + 16 * s + 8 * hh) * 2));
+  }
+  const float Dq = load_f32(rD, qrow * 4);
+  const float nl2 = load_f32(rL, qrow * 4);
+  floatx16 dqt[T::DBLK];  // dQ^T: lane = query, rows = d
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqt[b][i] = 0.f;
+
+  S st;
+  st.init(tid);
+  Offsets<D> off;
+  off.init(lane);
+  const float c2 = p.scale_log2;
+
+  const int k_end = CAUSAL ? min(N, q0 + T::BT) : N;
+  const int n_steps = (k_end + T::BS - 1) / T::BS;
+  // the ring carries K and V tiles; its statistics slots stay unused
+  st.template load<false>(rk, rv, rD, rL, 0, tid);
+  st.template store<false>(smem, tid);
+
+  for (int step = 0; step < n_steps; ++step) {
+    __syncthreads();
+    const int k_s = step * T::BS;
+    if (step + 1 < n_steps) st.template load<false>(rk, rv, rD, rL, k_s + T::BS, tid);
+    const typename S::lds_char* sk = smem + (step & 1) * T::SLOT_BYTES;
+    const typename S::lds_char* sv = sk + T::TILE_BYTES;
+
+    if (!CAUSAL || k_s <= qw0 + T::RW - 1) {
+      // S^T = K Q^T and dP^T = V dO^T: lane = query, register i = key
+      // k_s + 16 (i / 8) + 8 hh + i % 8.
+      floatx16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < T::KSTEPS; ++k)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sk + off.nat[k]),
+                                                   qf[k], s, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < T::KSTEPS; ++k)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sv + off.nat[k]),
+                                                    dof[k], dp, 0, 0, 0);
+      const bool edge = (CAUSAL && k_s + T::BS - 1 > qw0) || k_s + T::BS > N;
+      half8 dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nl2));
+        if (edge) {
+          const int kk = k_s + 16 * (i >> 3) + 8 * hh + (i & 7);
+          if ((CAUSAL && kk > qrow) || kk >= N) pv = 0.f;
+        }
+        dsf[i >> 3][i & 7] = (_Float16)(pv * (dp[i] - Dq));
+      }
+      // dQ^T += K^T dS^T (k = keys, two k-steps)
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const half8 a = tr_pair(sk, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
+          dqt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsf[ks], dqt[b], 0, 0, 0);
+        }
+    }
+    if (step + 1 < n_steps) st.template store<false>(smem + ((step + 1) & 1) * T::SLOT_BYTES, tid);
+  }
+
+  if (qrow < N) {
+    _Float16* dqr = p.dq + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        half8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (_Float16)(dqt[b][8 * g + e] * p.scale);
+        *reinterpret_cast<half8*>(dqr + 32 * b + 16 * g + 8 * hh) = w;
+      }
+  }
+}
+
+}  // namespace fmha

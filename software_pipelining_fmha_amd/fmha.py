@@ -1,6 +1,6 @@
 """Python binding of the C ABI in include/fmha.h (ctypes; argument
-marshalling only). Every step of the attention forward pass runs in
-libfmha.so's HIP kernels. There is no fallback: if the library is missing or
+marshalling only). Every step of the attention forward and backward passes
+runs in libfmha.so's HIP kernels. There is no fallback: if the library is missing or
 fails to load, every call here raises.
 
 PyTorch supplies device memory and the stream.
@@ -18,13 +18,14 @@ FMHA_ERR_INVALID_ARGUMENT = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_HIP = 3
 
-EXPORTS = ("fmha_fwd", "fmha_status_str", "fmha_query_tile", "fmha_key_tile")
+EXPORTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_bytes", "fmha_status_str",
+           "fmha_query_tile", "fmha_key_tile")
 
 
 class FmhaError(RuntimeError):
     def __init__(self, status: int):
         self.status = status
-        super().__init__("fmha_fwd failed: %s (status %d)" % (fmha_status_str(status), status))
+        super().__init__("fmha call failed: %s (status %d)" % (fmha_status_str(status), status))
 
 
 def lib():
@@ -38,6 +39,11 @@ def lib():
         l.fmha_fwd.restype = ctypes.c_int
         l.fmha_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float,
                                                                             ctypes.c_void_p]
+        l.fmha_bwd.restype = ctypes.c_int
+        l.fmha_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float,
+                                                                             ctypes.c_void_p]
+        l.fmha_bwd_workspace_bytes.restype = ctypes.c_size_t
+        l.fmha_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
         l.fmha_status_str.restype = ctypes.c_char_p
         l.fmha_status_str.argtypes = [ctypes.c_int]
         l.fmha_query_tile.restype = ctypes.c_int
@@ -56,6 +62,16 @@ def fmha_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
     """The C entry point, pointers as integers. Returns the status code."""
     return lib().fmha_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), int(causal),
                           float(scale), stream)
+
+
+def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, causal, scale, stream) -> int:
+    """The C entry point, pointers as integers. Returns the status code."""
+    return lib().fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, int(B), int(H), int(N), int(d),
+                          int(causal), float(scale), stream)
+
+
+def fmha_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib().fmha_bwd_workspace_bytes(int(B), int(H), int(N)))
 
 
 def fmha_status_str(status: int) -> str:
@@ -106,3 +122,46 @@ def forward(q, k, v, *, causal: bool = False, scale: float | None = None, out=No
     if st != FMHA_OK:
         raise FmhaError(st)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward on torch tensors: q, k, v, o, dout fp16 contiguous
+    [B, H, N, d] and lse fp32 [B, H, N] from the forward pass with the same
+    causal and scale. Returns (dq, dk, dv), fp16 [B, H, N, d]. The workspace
+    (fp32, at least 2*B*H*N elements) is allocated here unless given.
+    Launches on `stream` (default: torch's current stream) and does not
+    synchronise."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.float16 or t.dim() != 4 or t.shape != q.shape:
+            raise ValueError("%s must be fp16 shaped like q" % name)
+        if not t.is_contiguous() or not t.is_cuda or t.device != q.device:
+            raise ValueError("%s must be contiguous and on q's GPU" % name)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != torch.float16 or not t.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous fp16 tensors shaped like q")
+    if workspace is None:
+        workspace = torch.empty((2 * B * H * N,), dtype=torch.float32, device=q.device)
+    if (workspace.dtype != torch.float32 or not workspace.is_contiguous()
+            or workspace.numel() < 2 * B * H * N):
+        raise ValueError("workspace must be contiguous fp32 with at least 2*B*H*N elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = fmha_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      workspace.data_ptr(), B, H, N, d, causal, scale, handle)
+    if st != FMHA_OK:
+        raise FmhaError(st)
+    return dq, dk, dv

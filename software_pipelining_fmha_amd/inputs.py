@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module is shared by the HIP path's callers (tests, bench) and by the CPU
 oracle's callers. It draws numbers and picks rows. It holds no part of the
@@ -17,6 +17,11 @@ Recipe, per workload index c:
   [B, H, N, d], then round once to float16 (round-to-nearest-even);
 - the causal workload's K is fp16(3 * z), with the product taken in float32;
 - scale = float32(1 / sqrt(d)).
+Backward pass: the output gradient dO of workload c is one more float32
+standard_normal draw of the same shape, from
+numpy.random.default_rng(20260000 + c + DOUT_SEED_OFFSET), rounded once to
+float16. The pages give no backward workload, so it reuses the forward
+shapes.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ import numpy as np
 
 SEED_BASE = 20260000
 SAMPLE_SEED_XOR = 0x5EED
+DOUT_SEED_OFFSET = 500
 
 
 @dataclass(frozen=True)
@@ -81,6 +87,19 @@ def workload_inputs(index: int):
     w = WORKLOADS[index]
     q, k, v = draw_qkv(w.B, w.H, w.N, w.d, SEED_BASE + index, w.k_gain)
     return q, k, v, w.scale
+
+
+def draw_dout(B: int, H: int, N: int, d: int, seed: int):
+    """dO as a float16 array of shape [B,H,N,d]: one standard normal draw."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(size=(B, H, N, d), dtype=np.float32)
+    return z.astype(np.float16)
+
+
+def workload_dout(index: int):
+    """The output gradient for WORKLOADS[index]."""
+    w = WORKLOADS[index]
+    return draw_dout(w.B, w.H, w.N, w.d, SEED_BASE + index + DOUT_SEED_OFFSET)
 
 
 def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:

@@ -203,3 +203,44 @@ def test_bad_rows_rejected():
         oracle.fmha_bwd_rows(q, k, v, do, [[0, 0, 4]], [], causal=False, scale=0.5)
     with pytest.raises(RuntimeError):
         oracle.fmha_bwd_rows(q, k, v, do, [], [[0, 1, 0]], causal=False, scale=0.5)
+
+
+# --- root-sum-square tolerance scales ----------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rss_outputs_match_term_sums(causal):
+    """The optional tolerance scales: per element sqrt(sum_t a_t^2) over the
+    terms a_t of each gradient sum, and the D sensitivities
+    ds_q = scale * w_i * sum_j P_ij |k_jc| and
+    ds_k = scale * sqrt(sum_i (P_ij w_i q_ic)^2) with
+    w_i = sum_c |dO_ic| sum_j P_ij |v_jc|, all with P and dS from torch's
+    softmax (the GPU tests scale their tolerance by these). Values are
+    unchanged when the scales are requested."""
+    torch = pytest.importorskip("torch")
+    B, H, N, d = 1, 2, 19, 8
+    q, k, v, do = rand4(B, H, N, d, 121 + causal)
+    scale = np.float32(0.45)
+    plain = oracle.fmha_bwd_all(q, k, v, do, causal=causal, scale=scale)
+    dq, dk, dv, rq, rk, rv, sq, sk = oracle.fmha_bwd_all(q, k, v, do, causal=causal, scale=scale,
+                                                         rss=True)
+    for x, y in zip(plain, (dq, dk, dv)):
+        np.testing.assert_array_equal(x, y)
+    Q, K, V, DO = (torch.tensor(f64(x)) for x in (q, k, v, do))
+    s = float(scale) * (Q @ K.transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+    P = torch.softmax(s, dim=-1)
+    Dv = (DO * (P @ V)).sum(-1, keepdim=True)
+    dS = P * (DO @ V.transpose(-1, -2) - Dv)
+    sc = float(scale)
+    np.testing.assert_allclose(rv, torch.sqrt((P ** 2).transpose(-1, -2) @ DO ** 2).numpy(),
+                               rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(rk, sc * torch.sqrt((dS ** 2).transpose(-1, -2) @ Q ** 2).numpy(),
+                               rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(rq, sc * torch.sqrt((dS ** 2) @ K ** 2).numpy(),
+                               rtol=1e-12, atol=1e-15)
+    w = (DO.abs() * (P @ V.abs())).sum(-1, keepdim=True)
+    np.testing.assert_allclose(sq, (sc * w * (P @ K.abs())).numpy(), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(
+        sk, sc * torch.sqrt((P ** 2).transpose(-1, -2) @ (w ** 2 * Q ** 2)).numpy(),
+        rtol=1e-12, atol=1e-15)
