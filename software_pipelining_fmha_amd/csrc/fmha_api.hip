@@ -97,8 +97,9 @@ int launch_bwd(const fmha::BwdParams& prm, hipStream_t stream) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_delta_kernel<D>),
                                  dim3(delta_grid), dim3(256), args, 0, stream);
   if (e != hipSuccess) return FMHA_ERR_HIP;
+  static_assert(fmha::DkdvTile<D>::BT == T::BT, "both streaming kernels tile 128 rows");
   e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_dkdv_kernel<D, CAUSAL>),
-                      dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+                      dim3(prm.total_wg), dim3(fmha::DkdvTile<D>::THREADS), args, 0, stream);
   if (e != hipSuccess) return FMHA_ERR_HIP;
   e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_dq_kernel<D, CAUSAL>),
                       dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);

@@ -217,16 +217,52 @@ __device__ __forceinline__ int bwd_tile_id(int G) {
 // ---------------------------------------------------------------------------
 // 2. dK and dV: a workgroup owns 128 keys and streams the query tiles.
 // ---------------------------------------------------------------------------
+// Eight waves; waves w and w + 4 sit on one SIMD and share the 32 keys
+// k0 + 32 (w % 4). Wave w (the P wave) holds K and forms S = Q K^T, P and
+// dV^T += dO^T P; wave w + 4 (the dS wave) holds V and forms dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^T dS, taking P from the P wave through LDS.
+// Each step (32 queries) has two barrier-separated intervals in which one
+// wave of each SIMD feeds the matrix core while the other runs vector work:
+//   interval A_t: P wave  MFMA  dV_{t-1}, S_t     | dS wave VALU dS_{t-1}
+//   interval B_t: P wave  VALU  P_t (to LDS)      | dS wave MFMA dK_{t-1}, dP_t
+// Streamed steps sit in a 3-slot ring: step t+1 is loaded into registers at
+// the start of step t and written to LDS during B_t.
+template <int D>
+struct DkdvTile {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int PAIRS = 4;
+  static constexpr int RW = 32;                  // keys per wave pair
+  static constexpr int BT = PAIRS * RW;          // keys per workgroup
+  static constexpr int BS = 32;                  // queries per step
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = BS * D * 2;
+  static constexpr int TILE_CHUNKS = TILE_BYTES / 16;
+  static constexpr int STAT_BYTES = 2 * BS * 4;
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + STAT_BYTES;
+  static constexpr int SLOTS = 3;
+  static constexpr int P_BYTES = 2 * 1024;       // one pair's P (32 x 32 fp16)
+  static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES + PAIRS * P_BYTES;
+  static_assert(TILE_CHUNKS * 2 == THREADS || TILE_CHUNKS == THREADS, "staging covers a step");
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(BwdTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(BwdParams p) {
-  using T = BwdTile<D>;
-  using S = Stream<D>;
+__global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(BwdParams p) {
+  using T = DkdvTile<D>;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) half8 lds_half8;
+  typedef __attribute__((address_space(3))) intx4 lds_intx4;
+  typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
   __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
-  typename S::lds_char* const smem = (typename S::lds_char*)smem_raw;
+  lds_char* const smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool p_wave = wave < 4;
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int t = bwd_tile_id(p.total_wg);
@@ -234,121 +270,231 @@ __global__ __launch_bounds__(BwdTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(B
   const int kt = t - bh * p.n_t;  // causal: low key tiles see the most queries, so go first
   const int N = p.N;
   const int k0 = kt * T::BT;
-  const int kw0 = k0 + wave * T::RW;
+  const int kw0 = k0 + pair * T::RW;
   const int key = kw0 + l32;
 
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head, head_bytes);
   const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.ws + (size_t)bh * N, (uint32_t)N * 4u);
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.ws + p.rows + (size_t)bh * N, (uint32_t)N * 4u);
 
-  // K and V rows of this wave's keys: the B operands of S = Q K^T and
-  // dP = dO V^T (lane column = key, lane half hh holds d = 16 s + 8 hh ..).
-  half8 kf[T::KSTEPS], vf[T::KSTEPS];
+  // This wave's B operand rows: K (P wave) or V (dS wave) of its keys, lane
+  // column = key, lane half hh holding d = 16 s + 8 hh .. +7.
+  half8 bf[T::KSTEPS];
+  {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc((p_wave ? p.k : p.v) + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < T::KSTEPS; ++s) {
-    kf[s] = __builtin_bit_cast(half8, load16(rk, (key * D + 16 * s + 8 * hh) * 2));
-    vf[s] = __builtin_bit_cast(half8, load16(rv, (key * D + 16 * s + 8 * hh) * 2));
+    for (int s = 0; s < T::KSTEPS; ++s)
+      bf[s] = __builtin_bit_cast(half8, load16(rb, (key * D + 16 * s + 8 * hh) * 2));
   }
-  floatx16 dkt[T::DBLK], dvt[T::DBLK];  // dK^T, dV^T: lane = key, rows = d
+  floatx16 acc[T::DBLK];  // dV^T (P wave) or dK^T (dS wave): lane = key, rows = d
 #pragma unroll
   for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dkt[b][i] = dvt[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
 
-  S st;
-  st.init(tid);
   Offsets<D> off;
   off.init(lane);
   const float c2 = p.scale_log2;
 
+  // staging of one step: Q and dO rows (one 16-byte chunk per thread and
+  // tile at d = 128; at d = 64 the first half of the threads takes Q, the
+  // second dO) and the D and -lse*log2(e) values of its 32 queries
+  constexpr bool ONE_EACH = T::TILE_CHUNKS == T::THREADS;
+  const int chunk = ONE_EACH ? tid : tid % T::TILE_CHUNKS;
+  const int crow = chunk / T::CPR, ccol = chunk % T::CPR;
+  const int g_off = (crow * D + 8 * ccol) * 2;
+  const int l_off = crow * D * 2 + 16 * (ccol ^ bwd_swz<D>(crow));
+  const bool stage_q = ONE_EACH || tid < T::TILE_CHUNKS;
+  intx4 sa, sb;
+  float sst = 0.f;
+  auto stage_load = [&](int q_s) __attribute__((always_inline)) {
+    if (ONE_EACH) {
+      sa = load16(rq, q_s * D * 2 + g_off);
+      sb = load16(rdo, q_s * D * 2 + g_off);
+    } else {
+      sa = load16(stage_q ? rq : rdo, q_s * D * 2 + g_off);
+    }
+    if (tid < 2 * T::BS)
+      sst = tid < T::BS ? load_f32(rD, (q_s + tid) * 4) : load_f32(rL, (q_s + tid - T::BS) * 4);
+  };
+  auto stage_store = [&](lds_char* sl) __attribute__((always_inline)) {
+    if (ONE_EACH) {
+      *(lds_intx4*)(sl + l_off) = sa;
+      *(lds_intx4*)(sl + T::TILE_BYTES + l_off) = sb;
+    } else {
+      *(lds_intx4*)(sl + (stage_q ? 0 : T::TILE_BYTES) + l_off) = sa;
+    }
+    if (tid < 2 * T::BS) *(__attribute__((address_space(3))) float*)(sl + 2 * T::TILE_BYTES + 4 * tid) = sst;
+  };
+  lds_char* const pbuf = smem + T::SLOTS * T::SLOT_BYTES + pair * T::P_BYTES;
+
   const int q_begin = CAUSAL ? k0 : 0;
   const int n_steps = (N - q_begin + T::BS - 1) / T::BS;
-  st.template load<true>(rq, rdo, rD, rL, q_begin, tid);
-  st.template store<true>(smem, tid);
+  // a causal step entirely before the pair's first key contributes nothing
+  auto active = [&](int step) __attribute__((always_inline)) {
+    return step >= 0 && step < n_steps && (!CAUSAL || q_begin + step * T::BS + T::BS - 1 >= kw0);
+  };
+  auto stats = [&](const lds_char* sl, int which, floatx4 (&v)[4]) __attribute__((always_inline)) {
+    const lds_char* st = sl + 2 * T::TILE_BYTES + which * T::BS * 4;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = *(const lds_floatx4*)(st + 4 * (16 * (g >> 1) + 8 * hh + 4 * (g & 1)));
+  };
 
-  for (int step = 0; step < n_steps; ++step) {
-    __syncthreads();
-    const int q_s = q_begin + step * T::BS;
-    if (step + 1 < n_steps) st.template load<true>(rq, rdo, rD, rL, q_s + T::BS, tid);
-    const typename S::lds_char* sq = smem + (step & 1) * T::SLOT_BYTES;
-    const typename S::lds_char* sdo = sq + T::TILE_BYTES;
-    const typename S::lds_char* sstat = sq + 2 * T::TILE_BYTES;
+  floatx16 sc;     // S (P wave) or dP (dS wave) of the newest step
+  half8 w16[2];    // P (P wave) or dS (dS wave) of the previous step, fp16
 
-    // a causal step entirely before this wave's first key contributes nothing
-    if (!CAUSAL || q_s + T::BS - 1 >= kw0) {
-      // S = Q K^T and dP = dO V^T: lane = key, register i = query
-      // q_s + 16 (i / 8) + 8 hh + i % 8.
-      floatx16 s, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-#pragma unroll
-      for (int k = 0; k < T::KSTEPS; ++k)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sq + off.nat[k]),
-                                                   kf[k], s, 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < T::KSTEPS; ++k)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sdo + off.nat[k]),
-                                                    vf[k], dp, 0, 0, 0);
-      floatx4 dv4[4], nl4[4];  // D and -lse*log2(e) of the 16 queries
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
-        dv4[g] = *(const typename S::lds_floatx4*)(sstat + 4 * r);
-        nl4[g] = *(const typename S::lds_floatx4*)(sstat + 4 * (T::BS + r));
+  // Matrix-core interval: acc += (tile ct of step t-1)^T w16, then
+  // sc = (tile rt of step t) bf, 2 * DBLK + KSTEPS MFMAs in a fixed order,
+  // each LDS operand read OPERAND_AHEAD MFMAs before its use. It always runs
+  // whole: w16 is zero when step t-1 contributes nothing (the ring starts
+  // zeroed, so its operands are finite), and sc is simply unused when step t
+  // is inactive.
+  auto mfma_interval = [&](const lds_char* cs, int ct, const lds_char* rs, int rt)
+      __attribute__((always_inline)) {
+    constexpr int NC = 2 * T::DBLK, NM = NC + T::KSTEPS, AHEAD = OPERAND_AHEAD;
+    const lds_char* csrc = cs + ct * T::TILE_BYTES;
+    const lds_char* rsrc = rs + rt * T::TILE_BYTES;
+    auto operand = [&](int i) __attribute__((always_inline)) {
+      if (i < NC) {
+        const int b = i >> 1, ks = i & 1;
+        return tr_pair(csrc, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
       }
-      // mask: causal diagonal, ragged queries or keys
+      return *(const lds_half8*)(rsrc + off.nat[i - NC]);
+    };
+    half8 ring[AHEAD];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) ring[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 a = ring[i % AHEAD];
+      if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
+      if (i < NC) {
+        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w16[i & 1], acc[i >> 1], 0, 0, 0);
+      } else {
+        const floatx16 c = i == NC ? floatx16{} : sc;
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bf[i - NC], c, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto zero_w16 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w16[0][i] = w16[1][i] = (_Float16)0.f;
+  };
+
+  // One step t in the role of this wave. Slot indices are compile-time (U is
+  // t mod 3), so LDS addresses are a lane register plus an immediate.
+  auto p_step = [&](int t, auto u_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
+    lds_char* const cur = smem + U * T::SLOT_BYTES;
+    lds_char* const prev = smem + ((U + 2) % 3) * T::SLOT_BYTES;
+    lds_char* const next = smem + ((U + 1) % 3) * T::SLOT_BYTES;
+    if (t + 1 < n_steps) stage_load(q_begin + (t + 1) * T::BS);
+    // interval A: dV^T += dO^T P (step t-1), then S = Q K^T (step t)
+    __builtin_amdgcn_s_setprio(1);
+    mfma_interval(prev, 1, cur, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
+    // interval B: P = 2^(S c - lse log2 e) in fp16, to registers and LDS
+    if (active(t)) {
+      floatx4 nl[4];
+      stats(cur, 1, nl);
+      const int q_s = q_begin + t * T::BS;
       const bool edge = (CAUSAL && q_s < kw0 + T::RW - 1) || q_s + T::BS > N || kw0 + T::RW > N;
-      half8 pf[2], dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nl4[i >> 2][i & 3]));
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nl[i >> 2][i & 3]));
         if (edge) {
           const int q = q_s + 16 * (i >> 3) + 8 * hh + (i & 7);
           if ((CAUSAL && q < key) || q >= N || key >= N) pv = 0.f;
         }
-        pf[i >> 3][i & 7] = (_Float16)pv;
-        dsf[i >> 3][i & 7] = (_Float16)(pv * (dp[i] - dv4[i >> 2][i & 3]));
+        w16[i >> 3][i & 7] = (_Float16)pv;
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (k = queries, two k-steps)
-#pragma unroll
-      for (int b = 0; b < T::DBLK; ++b)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const half8 a = tr_pair(sdo, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
-          dvt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[ks], dvt[b], 0, 0, 0);
-        }
-#pragma unroll
-      for (int b = 0; b < T::DBLK; ++b)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const half8 a = tr_pair(sq, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
-          dkt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsf[ks], dkt[b], 0, 0, 0);
-        }
+      *(__attribute__((address_space(3))) half8*)(pbuf + 16 * lane) = w16[0];
+      *(__attribute__((address_space(3))) half8*)(pbuf + 1024 + 16 * lane) = w16[1];
+    } else {
+      zero_w16();
     }
-    if (step + 1 < n_steps) st.template store<true>(smem + ((step + 1) & 1) * T::SLOT_BYTES, tid);
+    if (t + 1 < n_steps) stage_store(next);
+    __syncthreads();
+  };
+  auto ds_step = [&](int t, auto u_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
+    lds_char* const cur = smem + U * T::SLOT_BYTES;
+    lds_char* const prev = smem + ((U + 2) % 3) * T::SLOT_BYTES;
+    lds_char* const next = smem + ((U + 1) % 3) * T::SLOT_BYTES;
+    if (t + 1 < n_steps) stage_load(q_begin + (t + 1) * T::BS);
+    // interval A: dS = P (dP - D) of step t-1, P from the P wave
+    if (active(t - 1)) {
+      floatx4 dd[4];
+      stats(prev, 0, dd);
+      const half8 p0 = *(const lds_half8*)(pbuf + 16 * lane);
+      const half8 p1 = *(const lds_half8*)(pbuf + 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+        w16[i >> 3][i & 7] = (_Float16)(pv * (sc[i] - dd[i >> 2][i & 3]));
+      }
+    } else {
+      zero_w16();
+    }
+    __syncthreads();
+    // interval B: dK^T += Q^T dS (step t-1), then dP = dO V^T (step t)
+    __builtin_amdgcn_s_setprio(1);
+    mfma_interval(prev, 0, cur, 1);
+    __builtin_amdgcn_s_setprio(0);
+    if (t + 1 < n_steps) stage_store(next);
+    __syncthreads();
+  };
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+
+  // prologue: the ring zeroed, then step 0 staged into slot 0
+  stage_load(q_begin);
+  for (int x = tid; x < T::SLOTS * T::SLOT_BYTES / 16; x += T::THREADS)
+    *(lds_intx4*)(smem + 16 * x) = intx4{0, 0, 0, 0};
+  __syncthreads();
+  stage_store(smem);
+  zero_w16();
+  __syncthreads();
+  // steps 0 .. n_steps (the last one only finishes step n_steps - 1)
+  if (p_wave) {
+    int t = 0;
+    for (; t + 2 <= n_steps; t += 3) {
+      p_step(t, U0{});
+      p_step(t + 1, U1{});
+      p_step(t + 2, U2{});
+    }
+    if (t <= n_steps) p_step(t, U0{});
+    if (t + 1 <= n_steps) p_step(t + 1, U1{});
+  } else {
+    int t = 0;
+    for (; t + 2 <= n_steps; t += 3) {
+      ds_step(t, U0{});
+      ds_step(t + 1, U1{});
+      ds_step(t + 2, U2{});
+    }
+    if (t <= n_steps) ds_step(t, U0{});
+    if (t + 1 <= n_steps) ds_step(t + 1, U1{});
   }
 
   // epilogue: register i of block b holds d = 32 b + 16 (i / 8) + 8 hh + i % 8
   if (key < N) {
-    _Float16* dkr = p.dk + head + (size_t)key * D;
-    _Float16* dvr = p.dv + head + (size_t)key * D;
+    _Float16* dst = (p_wave ? p.dv : p.dk) + head + (size_t)key * D;
+    const float f = p_wave ? 1.f : p.scale;
 #pragma unroll
     for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        half8 wk, wv;
+        half8 w;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          wk[e] = (_Float16)(dkt[b][8 * g + e] * p.scale);
-          wv[e] = (_Float16)dvt[b][8 * g + e];
-        }
-        *reinterpret_cast<half8*>(dkr + 32 * b + 16 * g + 8 * hh) = wk;
-        *reinterpret_cast<half8*>(dvr + 32 * b + 16 * g + 8 * hh) = wv;
+        for (int e = 0; e < 8; ++e) w[e] = (_Float16)(acc[b][8 * g + e] * f);
+        *reinterpret_cast<half8*>(dst + 32 * b + 16 * g + 8 * hh) = w;
       }
   }
 }
