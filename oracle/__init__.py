@@ -13,8 +13,9 @@ stages: QK^T, then softmax, then PV (Tawa, section III-D), and the
 load/mma/softmax/rescale tasks (PipeThreader, "core method"). This module
 only builds the C library and marshals arrays for it.
 
-Every function here is pinned by `tests/test_oracle.py` (forward) and
-`tests/test_oracle_bwd.py` (backward).
+Every function here is pinned by `tests/test_oracle.py` (forward),
+`tests/test_oracle_bwd.py` (backward) and `tests/test_oracle_fp8.py` (FP8
+inputs).
 """
 from __future__ import annotations
 
@@ -61,6 +62,15 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_fmha_fp8_rows.restype = ctypes.c_int
+        lib.oracle_fmha_fp8_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_e4m3_to_double.restype = None
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         lib.oracle_half_to_double.restype = None
         lib.oracle_half_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int64]
@@ -165,3 +175,50 @@ def fmha_bwd_all(q, k, v, dout, *, causal: bool, scale, threads: int | None = No
     out = fmha_bwd_rows(q, k, v, dout, rows, rows, causal=causal, scale=scale,
                         threads=threads, rss=rss)
     return tuple(x.reshape(B, H, N, d) for x in out)
+
+
+def e4m3_to_double(bits: np.ndarray) -> np.ndarray:
+    """Decode OCP FP8 E4M3 bytes (a uint8 array) to float64."""
+    a = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().oracle_e4m3_to_double(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def fmha_fp8_rows(q8, k8, v8, descales, rows, *, causal: bool, scale,
+                  threads: int | None = None, rss: bool = False):
+    """Attention rows for FP8 inputs: q8, k8, v8 are uint8 [B, H, N, d] arrays
+    of OCP E4M3 bytes, descales = (dq, dk, dv) per tensor. Returns
+    (o float64 [n, d], lse float64 [n]), plus the E4M3-weight tolerance
+    scales (rss_o [n, d], rss_l [n]) if rss=True."""
+    q8, k8, v8 = (np.ascontiguousarray(x, dtype=np.uint8) for x in (q8, k8, v8))
+    if q8.ndim != 4 or not (q8.shape == k8.shape == v8.shape):
+        raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
+    B, H, N, d = q8.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    ro = np.empty((n, d), dtype=np.float64) if rss else None
+    rl = np.empty((n,), dtype=np.float64) if rss else None
+    dq, dk, dv = (float(x) for x in descales)
+    st = _load().oracle_fmha_fp8_rows(
+        q8.ctypes.data, k8.ctypes.data, v8.ctypes.data, dq, dk, dv, B, H, N, d,
+        int(bool(causal)), float(scale), rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data,
+        ro.ctypes.data if rss else None, rl.ctypes.data if rss else None,
+        int(threads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_fmha_fp8_rows failed with status %d" % st)
+    return (o, lse, ro, rl) if rss else (o, lse)
+
+
+def fmha_fp8_all(q8, k8, v8, descales, *, causal: bool, scale, threads: int | None = None,
+                 rss: bool = False):
+    """Every row of the FP8 attention: (o [B,H,N,d], lse [B,H,N]) (+ scales)."""
+    B, H, N, d = q8.shape
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+    out = fmha_fp8_rows(q8, k8, v8, descales, rows, causal=causal, scale=scale,
+                        threads=threads, rss=rss)
+    shapes = [(B, H, N, d), (B, H, N), (B, H, N, d), (B, H, N)]
+    return tuple(x.reshape(sh) for x, sh in zip(out, shapes))

@@ -40,6 +40,13 @@
  *   dv_j  = sum_{i : j in J_i} P_ij * dO_i
  *
  * lse_i and o_i are recomputed here from q, k, v, never taken from a caller.
+ *
+ * FP8 inputs. Tawa (CGO'26), section V-D, also measures attention with FP8
+ * operands; the pages name no format. Here q, k, v may arrive as OCP FP8
+ * E4M3 bytes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent 0 is subnormal, S.1111.111 is NaN, there is no infinity) with one
+ * float descale per tensor: the value of byte x of q is descale_q * e4m3(x).
+ * The attention is then the same definition on those values.
  */
 #include <math.h>
 #include <pthread.h>
@@ -584,4 +591,196 @@ int oracle_fmha_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     free(D);
     free(W);
     return st;
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP8 (OCP E4M3) inputs                                                      */
+/* ------------------------------------------------------------------------- */
+
+/* OCP FP8 E4M3 -> binary64, exact. */
+static double decode_e4m3(uint8_t x)
+{
+    const int sign = x >> 7;
+    const int expo = (x >> 3) & 0xf;
+    const int frac = x & 0x7;
+    double v;
+    if (expo == 0xf && frac == 0x7)
+        v = NAN;
+    else if (expo == 0)
+        v = ldexp((double)frac, -9);                  /* 0.frac * 2^-6 */
+    else
+        v = ldexp((double)(frac | 0x8), expo - 10);   /* 1.frac * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+void oracle_e4m3_to_double(const uint8_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = decode_e4m3(src[i]);
+}
+
+typedef struct {
+    const uint8_t *q, *k, *v;
+    double dq, dk, dv; /* descales */
+    int64_t H, N, d;
+    int causal;
+    double scale;
+    const int64_t *rows;
+    double *o, *lse, *rss_o, *rss_l;
+    int64_t begin, end;
+    int status;
+} f8job_t;
+
+static double g_e4m3[256];
+static pthread_once_t g_e4m3_once = PTHREAD_ONCE_INIT;
+
+static void build_e4m3_table(void)
+{
+    for (int i = 0; i < 256; ++i)
+        g_e4m3[i] = decode_e4m3((uint8_t)i);
+}
+
+/* One query row of the attention on the decoded, descaled values (the same
+ * definition as one_row). If rss_o / rss_l are not NULL they receive a
+ * tolerance scale for a kernel that rounds each weight P_ij to E4M3
+ * (relative error <= 2^-4, absolute <= 2^-10 of the largest weight below the
+ * normal range): with e_j = max(2^-4 P_ij, 2^-10 P_max),
+ *   rss_o[c] = sqrt(sum_j e_j^2 (v_jc - o_c)^2),  rss_l = sqrt(sum_j e_j^2). */
+static void one_row_fp8(const f8job_t *jb, int64_t r, double *s)
+{
+    const int64_t b = jb->rows[3 * r + 0];
+    const int64_t h = jb->rows[3 * r + 1];
+    const int64_t i = jb->rows[3 * r + 2];
+    const int64_t N = jb->N, d = jb->d;
+    const int64_t head = (b * jb->H + h) * N * d;
+    const uint8_t *qi = jb->q + head + i * d;
+    const uint8_t *kh = jb->k + head;
+    const uint8_t *vh = jb->v + head;
+    double *o = jb->o + r * d;
+    const int64_t nvis = jb->causal ? i + 1 : N;
+
+    for (int64_t j = 0; j < nvis; ++j) {
+        const uint8_t *kj = kh + j * d;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += (jb->dq * g_e4m3[qi[c]]) * (jb->dk * g_e4m3[kj[c]]);
+        s[j] = jb->scale * dot;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j)
+        if (s[j] > m)
+            m = s[j];
+    double l = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+        o[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double e = exp(s[j] - m);
+        const uint8_t *vj = vh + j * d;
+        l += e;
+        for (int64_t c = 0; c < d; ++c)
+            o[c] += e * (jb->dv * g_e4m3[vj[c]]);
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o[c] /= l;
+    jb->lse[r] = m + log(l);
+
+    if (jb->rss_o) {
+        double *ro = jb->rss_o + r * d;
+        double rl = 0.0;
+        const double pmax = 1.0 / l; /* the largest weight: exp(m - m) / l */
+        for (int64_t c = 0; c < d; ++c)
+            ro[c] = 0.0;
+        for (int64_t j = 0; j < nvis; ++j) {
+            const double P = exp(s[j] - m) / l;
+            const double e = fmax(0.0625 * P, 0.0009765625 * pmax);
+            const uint8_t *vj = vh + j * d;
+            rl += e * e;
+            for (int64_t c = 0; c < d; ++c) {
+                const double t = e * (jb->dv * g_e4m3[vj[c]] - o[c]);
+                ro[c] += t * t;
+            }
+        }
+        for (int64_t c = 0; c < d; ++c)
+            ro[c] = sqrt(ro[c]);
+        jb->rss_l[r] = sqrt(rl);
+    }
+}
+
+static void *fp8_worker(void *arg)
+{
+    f8job_t *jb = (f8job_t *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)jb->N);
+    if (!s) {
+        jb->status = 3;
+        return NULL;
+    }
+    for (int64_t r = jb->begin; r < jb->end; ++r)
+        one_row_fp8(jb, r, s);
+    free(s);
+    return NULL;
+}
+
+/*
+ * Attention rows for FP8 inputs.
+ *   q, k, v         : OCP E4M3 bytes, [B, H, N, d] contiguous
+ *   dq, dk, dv      : per-tensor descales (value = descale * e4m3(byte))
+ *   rows, n_rows    : (b, h, i) triples
+ *   o, lse          : n_rows x d and n_rows doubles (output)
+ *   rss_o, rss_l    : NULL, or like o and lse: the E4M3-weight tolerance
+ *                     scales described at one_row_fp8
+ * Returns 0 on success, 1 on a bad argument, 3 if memory or a thread could
+ * not be had.
+ */
+int oracle_fmha_fp8_rows(const uint8_t *q, const uint8_t *k, const uint8_t *v, double dq,
+                         double dk, double dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int causal, double scale, const int64_t *rows, int64_t n_rows,
+                         double *o, double *lse, double *rss_o, double *rss_l, int threads)
+{
+    if (!q || !k || !v || !rows || !o || !lse || B <= 0 || H <= 0 || N <= 0 || d <= 0 ||
+        n_rows < 0 || threads < 1 || ((rss_o == NULL) != (rss_l == NULL)))
+        return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t *t = rows + 3 * r;
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= N)
+            return 1;
+    }
+    pthread_once(&g_e4m3_once, build_e4m3_table);
+    if (n_rows == 0)
+        return 0;
+    if (threads > n_rows)
+        threads = (int)n_rows;
+    f8job_t *jobs = (f8job_t *)calloc((size_t)threads, sizeof(f8job_t));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    int *started = (int *)calloc((size_t)threads, sizeof(int));
+    if (!jobs || !tids || !started) {
+        free(jobs);
+        free(tids);
+        free(started);
+        return 3;
+    }
+    int status = 0;
+    for (int t = 0; t < threads; ++t) {
+        f8job_t *jb = &jobs[t];
+        jb->q = q; jb->k = k; jb->v = v;
+        jb->dq = dq; jb->dk = dk; jb->dv = dv;
+        jb->H = H; jb->N = N; jb->d = d;
+        jb->causal = causal; jb->scale = scale;
+        jb->rows = rows; jb->o = o; jb->lse = lse; jb->rss_o = rss_o; jb->rss_l = rss_l;
+        jb->begin = n_rows * t / threads;
+        jb->end = n_rows * (t + 1) / threads;
+        if (threads > 1 && pthread_create(&tids[t], NULL, fp8_worker, jb) == 0)
+            started[t] = 1;
+        else
+            fp8_worker(jb);
+    }
+    for (int t = 0; t < threads; ++t) {
+        if (started[t])
+            pthread_join(tids[t], NULL);
+        if (jobs[t].status)
+            status = jobs[t].status;
+    }
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
 }

@@ -17,6 +17,11 @@ Recipe, per workload index c:
   [B, H, N, d], then round once to float16 (round-to-nearest-even);
 - the causal workload's K is fp16(3 * z), with the product taken in float32;
 - scale = float32(1 / sqrt(d)).
+FP8 inputs (FP8_WORKLOADS): the same float32 draws as the FP16 workload of
+the same shape, each tensor quantized on its own to OCP FP8 E4M3 with
+descale = float32(amax / 448) (amax over the whole tensor) and bytes =
+e4m3(RNE(x / descale)), the division in float32. Tawa (CGO'26), section V-D,
+measures FP8 attention at batch 4, head dim 128, L from 1K to 16K.
 Backward pass: the output gradient dO of workload c is one more float32
 standard_normal draw of the same shape, from
 numpy.random.default_rng(20260000 + c + DOUT_SEED_OFFSET), rounded once to
@@ -67,6 +72,16 @@ WORKLOADS = (
 )
 HEADLINE = 3
 
+FP8_WORKLOADS = (
+    Workload("fp8_tiny_b1h1n128d128", 1, 1, 128, 128, False),
+    Workload("fp8_b4h32n1024d128", 4, 32, 1024, 128, False),
+    Workload("fp8_b4h32n4096d128", 4, 32, 4096, 128, False, sampled_rows=256),
+    Workload("fp8_b4h32n16384d128", 4, 32, 16384, 128, False, sampled_rows=256),
+    Workload("fp8_causal_b4h32n8192d128_k3", 4, 32, 8192, 128, True, k_gain=3.0,
+             sampled_rows=256),
+)
+FP8_SEED_OFFSET = 700
+
 
 def draw_qkv(B: int, H: int, N: int, d: int, seed: int, k_gain: float = 1.0):
     """Q, K, V as float16 arrays of shape [B,H,N,d], drawn in that order."""
@@ -80,6 +95,55 @@ def draw_qkv(B: int, H: int, N: int, d: int, seed: int, k_gain: float = 1.0):
         out.append(z.astype(np.float16))
         del z
     return tuple(out)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """(bytes uint8, descale float32): x ~= descale * e4m3(bytes), per tensor."""
+    import torch
+
+    amax = float(np.abs(x).max())
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    y = (x.astype(np.float32) / descale).astype(np.float32)
+    b = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(b), descale
+
+
+def draw_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, k_gain: float = 1.0):
+    """FP8 Q, K, V: ((q8, k8, v8) uint8 arrays, (dq, dk, dv) descales). The
+    float32 draws are those of draw_qkv with the same arguments."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    bytes_, scales = [], []
+    for name in ("q", "k", "v"):
+        z = rng.standard_normal(size=shape, dtype=np.float32)
+        if name == "k" and k_gain != 1.0:
+            z *= np.float32(k_gain)
+        b, sc = quantize_e4m3(z)
+        del z
+        bytes_.append(b)
+        scales.append(sc)
+    return tuple(bytes_), tuple(scales)
+
+
+def fp8_workload_inputs(index: int):
+    """((q8, k8, v8), (dq, dk, dv), scale) for FP8_WORKLOADS[index]."""
+    w = FP8_WORKLOADS[index]
+    b, sc = draw_qkv_fp8(w.B, w.H, w.N, w.d, SEED_BASE + FP8_SEED_OFFSET + index, w.k_gain)
+    return b, sc, w.scale
+
+
+def fp8_workload_rows(index: int) -> np.ndarray:
+    """The (b,h,i) triples the oracle checks for FP8_WORKLOADS[index]."""
+    w = FP8_WORKLOADS[index]
+    seed = (SEED_BASE + FP8_SEED_OFFSET + index) ^ SAMPLE_SEED_XOR
+    if w.sampled_rows == 0:
+        b, h, i = np.meshgrid(np.arange(w.B), np.arange(w.H), np.arange(w.N), indexing="ij")
+        return np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int64)
+    rows = sample_rows(w.B, w.H, w.N, w.sampled_rows, seed)
+    if w.causal:
+        extra = boundary_rows(w.B, w.H, w.N, 4, seed + 1)
+        rows = np.unique(np.concatenate([rows, extra]), axis=0)
+    return rows
 
 
 def workload_inputs(index: int):

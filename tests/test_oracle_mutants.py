@@ -26,7 +26,8 @@ MUTANTS = {
     "lse without max": ("jb->lse[r] = m + log(l);", "jb->lse[r] = log(l);"),
     "no normalisation": ("o[c] /= l;", "o[c] /= 1.0;"),
     "values in reverse key order": ("vh + j * d", "vh + (nvis - 1 - j) * d"),
-    "batch and head swapped": ("(b * jb->H + h)", "(h * jb->B + b)"),
+    "batch and head swapped": ("const int64_t head = (b * jb->H + h) * N * d;\n    const uint16_t *qi",
+                               "const int64_t head = (h * jb->B + b) * N * d;\n    const uint16_t *qi"),
     "wrong query row": ("jb->q + head + i * d", "jb->q + head + (N - 1 - i) * d"),
     "half exponent bias": ("expo - 25", "expo - 24"),
     "subnormal scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
@@ -49,6 +50,26 @@ BWD_MUTANTS = {
     "bwd: weights without lse": ("exp(a->scale * dot - lse[i])", "exp(a->scale * dot)"),
     "bwd: query gradient from values": ("dq[c] += dS * g_half[kj[c]];", "dq[c] += dS * g_half[vj[c]];"),
 }
+
+
+# Slips in the FP8 path; each must fail a pin of test_oracle_fp8.py.
+FP8_MUTANTS = {
+    "fp8: exponent bias 8": ("ldexp((double)(frac | 0x8), expo - 10)",
+                             "ldexp((double)(frac | 0x8), expo - 11)"),
+    "fp8: subnormal scale": ("ldexp((double)frac, -9)", "ldexp((double)frac, -10)"),
+    "fp8: NaN rule dropped": ("if (expo == 0xf && frac == 0x7)", "if (0)"),
+    "fp8: v descale dropped": ("o[c] += e * (jb->dv * g_e4m3[vj[c]]);", "o[c] += e * g_e4m3[vj[c]];"),
+    "fp8: q descale squared": ("dot += (jb->dq * g_e4m3[qi[c]])", "dot += (jb->dq * jb->dq * g_e4m3[qi[c]])"),
+}
+
+
+def _fp8_pin_calls():
+    from tests import test_oracle_fp8 as fp
+    return [
+        fp.test_e4m3_decode_matches_torch,
+        lambda: fp.test_matches_fp16_oracle_on_exact_inputs(False, (0.25, 2.0, 0.5)),
+        lambda: fp.test_matches_fp16_oracle_on_exact_inputs(True, (1.0, 1.0, 1.0)),
+    ]
 
 
 def _bwd_pin_calls():
@@ -95,7 +116,8 @@ def _build_mutant(tmp_path, name, old, new):
     return str(so)
 
 
-EXPORTS = ("oracle_fmha_rows", "oracle_fmha_bwd_rows", "oracle_half_to_double")
+EXPORTS = ("oracle_fmha_rows", "oracle_fmha_bwd_rows", "oracle_half_to_double",
+           "oracle_fmha_fp8_rows", "oracle_e4m3_to_double")
 
 
 def _swap_in(so, monkeypatch):
@@ -107,13 +129,22 @@ def _swap_in(so, monkeypatch):
     monkeypatch.setattr(oracle, "_lib", lib)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BWD_MUTANTS))
+ALL_MUTANTS = {**MUTANTS, **BWD_MUTANTS, **FP8_MUTANTS}
+
+
+def _calls_for(name):
+    if name in MUTANTS:
+        return _pin_calls()
+    return _bwd_pin_calls() if name in BWD_MUTANTS else _fp8_pin_calls()
+
+
+@pytest.mark.parametrize("name", sorted(ALL_MUTANTS))
 def test_mutant_is_caught(name, tmp_path, monkeypatch):
-    old, new = MUTANTS[name] if name in MUTANTS else BWD_MUTANTS[name]
+    old, new = ALL_MUTANTS[name]
     so = _build_mutant(tmp_path, name, old, new)
     _swap_in(so, monkeypatch)
     failures = 0
-    for call in (_pin_calls() if name in MUTANTS else _bwd_pin_calls()):
+    for call in _calls_for(name):
         try:
             call()
         except (AssertionError, RuntimeError, FloatingPointError):
@@ -125,5 +156,5 @@ def test_unmutated_copy_passes_every_pin(tmp_path, monkeypatch):
     """Control: the same build of the untouched source fails no pin."""
     so = _build_mutant(tmp_path, "identity", "exp(s[j] - m)", "exp(s[j] - m)")
     _swap_in(so, monkeypatch)
-    for call in _pin_calls() + _bwd_pin_calls():
+    for call in _pin_calls() + _bwd_pin_calls() + _fp8_pin_calls():
         call()
