@@ -15,6 +15,10 @@ launch time from HIP events on the launch stream) and, on rank 0, the CPU
 oracle timed on a bounded row sample. The oracle's rows also check the
 timed output.
 
+--dtype fp8 times fmha_fwd_fp8 instead, on the FP8 workloads (the same
+shapes and draws quantized per tensor to OCP E4M3), against the MFMA's dense
+FP8 peak.
+
 --pass bwd times one fmha_bwd call per step instead (its three kernels: the
 row dot products D, dK/dV, dQ) on the same workload plus a seeded output
 gradient, after one untimed forward pass that supplies O and lse. It counts
@@ -41,15 +45,25 @@ from software_pipelining_fmha_amd import inputs  # noqa: E402
 
 METRIC = "FMHA fwd TFLOPS (fp16, B4 H32 d128, N=16384) and % of MFMA peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 KERNEL_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_kernel.hpp",
                   "software_pipelining_fmha_amd/csrc/fmha_api.hip")
 BWD_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_bwd_kernel.hpp",)
+FP8_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_fp8_kernel.hpp",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fmha_fwd_b4h32n16384d128.txt")
 
 
 def kernel_digest() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fp8_digest() -> str:
+    h = hashlib.sha256()
+    for rel in FP8_SOURCES + KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -224,6 +238,89 @@ def bench_bwd(args, w, idx, q, k, v, scale, tq, tk, tv, dev, stream):
     return 0
 
 
+def bench_fp8(args) -> int:
+    import torch
+
+    from software_pipelining_fmha_amd import fmha
+
+    names = [w.name for w in inputs.FP8_WORKLOADS]
+    name = args.workload if args.workload in names else "fp8_" + args.workload
+    if name not in names:
+        print("no FP8 workload named %s (have %s)" % (args.workload, ", ".join(names)), file=sys.stderr)
+        return 2
+    idx = names.index(name)
+    w = inputs.FP8_WORKLOADS[idx]
+    dev = torch.device("cuda:0")
+    (q8, k8, v8), sc, scale = inputs.fp8_workload_inputs(idx)
+    tq, tk, tv = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fmha.forward_fp8(tq, tk, tv, sc, causal=w.causal, scale=float(scale), out=o, lse=lse,
+                         stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    avg_ms = float(np.mean(launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": "FMHA fwd TFLOPS (fp8 e4m3, %s) and %% of MFMA peak" % w.name,
+        "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "k_gain": w.k_gain, "layout": "BHNd", "flops_per_step": w.flops,
+                   "seed": inputs.SEED_BASE + inputs.FP8_SEED_OFFSET + idx,
+                   "descales": [float(x) for x in sc]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "kernel_ms_avg": round(avg_ms, 4), "kernel_ms_min": round(min(launch_ms), 4),
+                     "kernel_digest": fp8_digest()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = cpu_threads()
+        rows = inputs.fp8_workload_rows(idx) if w.sampled_rows else inputs.sample_rows(
+            w.B, w.H, w.N, 256, 4545 + idx)
+        t1 = time.perf_counter()
+        ref = oracle.fmha_fp8_rows(q8, k8, v8, sc, rows, causal=w.causal, scale=scale,
+                                   threads=threads, rss=True)
+        dt = time.perf_counter() - t1
+        b, h, i = rows.T
+        og = o.cpu().numpy()[b, h, i].astype(np.float64)
+        lg = lse.cpu().numpy()[b, h, i].astype(np.float64)
+        e = 2.0 ** -11
+        bar_o = 7 * ref[2] + e * ref[4] + 2.0 ** -10 * np.abs(ref[0]) + 2.0 ** -16
+        bar_l = 7 * ref[3] + e * ref[5] + 2.0 ** -20 * np.abs(ref[1]) + 2.0 ** -16
+        worst = max(float((np.abs(og - ref[0]) / bar_o).max()), float((np.abs(lg - ref[1]) / bar_l).max()))
+        vis = (rows[:, 2] + 1).astype(np.float64) if w.causal else np.full(len(rows), float(w.N))
+        result["cpu_baseline"] = {
+            "value": float((4.0 * w.d * vis).sum()) / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d seeded (b,h,i) rows of %s with tolerance scales; %.1f s wall" % (len(rows), w.name, dt)}
+        result["parity"] = {"rows": int(len(rows)), "max_err_over_bar": worst, "pass": bool(worst <= 1.0)}
+    print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        return 1
+    return 0
+
+
 def copy_calibration(mib: int, steps: int) -> int:
     """A plain copy kernel of known size: `steps` launches that each read and
     write mib MiB."""
@@ -247,7 +344,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=inputs.WORKLOADS[inputs.HEADLINE].name,
-                    choices=[w.name for w in inputs.WORKLOADS])
+                    choices=[w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.FP8_WORKLOADS])
+    ap.add_argument("--dtype", choices=["f16", "fp8"], default="f16",
+                    help="f16 (default) or the FP8 (E4M3) forward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -274,6 +373,11 @@ def main(argv=None) -> int:
     fmha.lib()  # fail loudly before any work if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dtype == "fp8":
+        if args.which != "fwd":
+            print("the FP8 path is forward only", file=sys.stderr)
+            return 2
+        return bench_fp8(args)
     w = next(x for x in inputs.WORKLOADS if x.name == args.workload)
     idx = inputs.WORKLOADS.index(w)
     q, k, v, scale = inputs.workload_inputs(idx)

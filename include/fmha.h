@@ -71,6 +71,26 @@ int fmha_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int H, int N, int d, int causal, float scale, void *stream);
 
 /*
+ * fmha_fwd_fp8 - the forward pass above with FP8 inputs (Tawa, CGO'26,
+ * section V-D, measures FP8 attention; the pages name no format, so the OCP
+ * FP8 E4M3 encoding with one descale per tensor is the reading taken).
+ *
+ * q, k, v    : device pointers to OCP E4M3 bytes, contiguous [B, H, N, d]. The
+ *              value of byte x of q is descale_q * e4m3(x) (likewise k, v).
+ * descale_*  : per-tensor descales, finite and > 0.
+ * o, lse     : as for fmha_fwd (o binary16, lse float32 natural-log logsumexp
+ *              of scale * q_i . k_j over the visible keys, descales included).
+ * d          : 128 (the only head dim of this path).
+ * Other arguments, ownership and errors as for fmha_fwd. Both products run on
+ * the FP8 matrix core with fp32 accumulation; the softmax weights are rounded
+ * to E4M3 before the second product, and the row sums add exactly those
+ * rounded weights.
+ */
+int fmha_fwd_fp8(const void *q, const void *k, const void *v, float descale_q, float descale_k,
+                 float descale_v, void *o, float *lse, int B, int H, int N, int d, int causal,
+                 float scale, void *stream);
+
+/*
  * fmha_bwd - enqueue the attention backward pass on `stream`.
  *
  * The gradients of the scalar sum_{b,h,i,c} dout[b,h,i,c] * o[b,h,i,c] with

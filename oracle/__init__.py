@@ -68,7 +68,8 @@ def _load():
             ctypes.c_double, ctypes.c_double, ctypes.c_double,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_e4m3_to_double.restype = None
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         lib.oracle_half_to_double.restype = None
@@ -189,8 +190,10 @@ def fmha_fp8_rows(q8, k8, v8, descales, rows, *, causal: bool, scale,
                   threads: int | None = None, rss: bool = False):
     """Attention rows for FP8 inputs: q8, k8, v8 are uint8 [B, H, N, d] arrays
     of OCP E4M3 bytes, descales = (dq, dk, dv) per tensor. Returns
-    (o float64 [n, d], lse float64 [n]), plus the E4M3-weight tolerance
-    scales (rss_o [n, d], rss_l [n]) if rss=True."""
+    (o float64 [n, d], lse float64 [n]), plus the tolerance scales
+    (rss_o [n, d], rss_l [n], sc_o [n, d], sc_l [n]) if rss=True: rss_* for
+    weights rounded to E4M3, sc_* for score errors proportional to the sum of
+    the magnitudes of the products (see fmha_oracle.c)."""
     q8, k8, v8 = (np.ascontiguousarray(x, dtype=np.uint8) for x in (q8, k8, v8))
     if q8.ndim != 4 or not (q8.shape == k8.shape == v8.shape):
         raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
@@ -199,17 +202,16 @@ def fmha_fp8_rows(q8, k8, v8, descales, rows, *, causal: bool, scale,
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    ro = np.empty((n, d), dtype=np.float64) if rss else None
-    rl = np.empty((n,), dtype=np.float64) if rss else None
+    extra = [np.empty((n, d)), np.empty((n,)), np.empty((n, d)), np.empty((n,))] if rss else []
+    ptrs = [x.ctypes.data for x in extra] if rss else [None] * 4
     dq, dk, dv = (float(x) for x in descales)
     st = _load().oracle_fmha_fp8_rows(
         q8.ctypes.data, k8.ctypes.data, v8.ctypes.data, dq, dk, dv, B, H, N, d,
         int(bool(causal)), float(scale), rows.ctypes.data, n, o.ctypes.data, lse.ctypes.data,
-        ro.ctypes.data if rss else None, rl.ctypes.data if rss else None,
-        int(threads or default_threads()))
+        *ptrs, int(threads or default_threads()))
     if st != 0:
         raise RuntimeError("oracle_fmha_fp8_rows failed with status %d" % st)
-    return (o, lse, ro, rl) if rss else (o, lse)
+    return (o, lse, *extra) if rss else (o, lse)
 
 
 def fmha_fp8_all(q8, k8, v8, descales, *, causal: bool, scale, threads: int | None = None,
@@ -220,5 +222,5 @@ def fmha_fp8_all(q8, k8, v8, descales, *, causal: bool, scale, threads: int | No
     rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
     out = fmha_fp8_rows(q8, k8, v8, descales, rows, causal=causal, scale=scale,
                         threads=threads, rss=rss)
-    shapes = [(B, H, N, d), (B, H, N), (B, H, N, d), (B, H, N)]
+    shapes = [(B, H, N, d), (B, H, N)] * 3
     return tuple(x.reshape(sh) for x, sh in zip(out, shapes))

@@ -626,7 +626,7 @@ typedef struct {
     int causal;
     double scale;
     const int64_t *rows;
-    double *o, *lse, *rss_o, *rss_l;
+    double *o, *lse, *rss_o, *rss_l, *sc_o, *sc_l;
     int64_t begin, end;
     int status;
 } f8job_t;
@@ -645,7 +645,10 @@ static void build_e4m3_table(void)
  * tolerance scale for a kernel that rounds each weight P_ij to E4M3
  * (relative error <= 2^-4, absolute <= 2^-10 of the largest weight below the
  * normal range): with e_j = max(2^-4 P_ij, 2^-10 P_max),
- *   rss_o[c] = sqrt(sum_j e_j^2 (v_jc - o_c)^2),  rss_l = sqrt(sum_j e_j^2). */
+ *   rss_o[c] = sqrt(sum_j e_j^2 (v_jc - o_c)^2),  rss_l = sqrt(sum_j e_j^2);
+ * and sc_o / sc_l a scale for errors in the scores proportional to
+ * a_j = scale * sum_c |q_c k_jc| (the sum of the magnitudes of the products):
+ *   sc_o[c] = sum_j P_ij a_j |v_jc - o_c|,  sc_l = sum_j P_ij a_j. */
 static void one_row_fp8(const f8job_t *jb, int64_t r, double *s)
 {
     const int64_t b = jb->rows[3 * r + 0];
@@ -703,6 +706,24 @@ static void one_row_fp8(const f8job_t *jb, int64_t r, double *s)
         for (int64_t c = 0; c < d; ++c)
             ro[c] = sqrt(ro[c]);
         jb->rss_l[r] = sqrt(rl);
+
+        double *so = jb->sc_o + r * d;
+        double sl = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            so[c] = 0.0;
+        for (int64_t j = 0; j < nvis; ++j) {
+            const double P = exp(s[j] - m) / l;
+            const uint8_t *kj = kh + j * d;
+            const uint8_t *vj = vh + j * d;
+            double a = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                a += fabs((jb->dq * g_e4m3[qi[c]]) * (jb->dk * g_e4m3[kj[c]]));
+            a *= jb->scale;
+            sl += P * a;
+            for (int64_t c = 0; c < d; ++c)
+                so[c] += P * a * fabs(jb->dv * g_e4m3[vj[c]] - o[c]);
+        }
+        jb->sc_l[r] = sl;
     }
 }
 
@@ -726,18 +747,22 @@ static void *fp8_worker(void *arg)
  *   dq, dk, dv      : per-tensor descales (value = descale * e4m3(byte))
  *   rows, n_rows    : (b, h, i) triples
  *   o, lse          : n_rows x d and n_rows doubles (output)
- *   rss_o, rss_l    : NULL, or like o and lse: the E4M3-weight tolerance
- *                     scales described at one_row_fp8
+ *   rss_o, rss_l,
+ *   sc_o, sc_l      : all NULL, or like o, lse, o, lse: the tolerance scales
+ *                     described at one_row_fp8
  * Returns 0 on success, 1 on a bad argument, 3 if memory or a thread could
  * not be had.
  */
 int oracle_fmha_fp8_rows(const uint8_t *q, const uint8_t *k, const uint8_t *v, double dq,
                          double dk, double dv, int64_t B, int64_t H, int64_t N, int64_t d,
                          int causal, double scale, const int64_t *rows, int64_t n_rows,
-                         double *o, double *lse, double *rss_o, double *rss_l, int threads)
+                         double *o, double *lse, double *rss_o, double *rss_l, double *sc_o,
+                         double *sc_l, int threads)
 {
+    const int scales = rss_o != NULL;
     if (!q || !k || !v || !rows || !o || !lse || B <= 0 || H <= 0 || N <= 0 || d <= 0 ||
-        n_rows < 0 || threads < 1 || ((rss_o == NULL) != (rss_l == NULL)))
+        n_rows < 0 || threads < 1 || scales != (rss_l != NULL) || scales != (sc_o != NULL) ||
+        scales != (sc_l != NULL))
         return 1;
     for (int64_t r = 0; r < n_rows; ++r) {
         const int64_t *t = rows + 3 * r;
@@ -766,6 +791,7 @@ int oracle_fmha_fp8_rows(const uint8_t *q, const uint8_t *k, const uint8_t *v, d
         jb->H = H; jb->N = N; jb->d = d;
         jb->causal = causal; jb->scale = scale;
         jb->rows = rows; jb->o = o; jb->lse = lse; jb->rss_o = rss_o; jb->rss_l = rss_l;
+        jb->sc_o = sc_o; jb->sc_l = sc_l;
         jb->begin = n_rows * t / threads;
         jb->end = n_rows * (t + 1) / threads;
         if (threads > 1 && pthread_create(&tids[t], NULL, fp8_worker, jb) == 0)

@@ -8,6 +8,7 @@
 
 #include "fmha.h"
 #include "fmha_bwd_kernel.hpp"
+#include "fmha_fwd_fp8_kernel.hpp"
 #include "fmha_fwd_kernel.hpp"
 
 namespace {
@@ -171,6 +172,51 @@ extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 64) return causal ? launch_bwd<64, true>(prm, s) : launch_bwd<64, false>(prm, s);
   return causal ? launch_bwd<128, true>(prm, s) : launch_bwd<128, false>(prm, s);
+}
+
+extern "C" int fmha_fwd_fp8(const void* q, const void* k, const void* v, float descale_q,
+                            float descale_k, float descale_v, void* o, float* lse, int B, int H,
+                            int N, int d, int causal, float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || N == 0) return FMHA_OK;
+  if (!q || !k || !v || !o || !lse) return FMHA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale) || !std::isfinite(descale_q) || !std::isfinite(descale_k) ||
+      !std::isfinite(descale_v))
+    return FMHA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !(descale_q > 0.f) || !(descale_k > 0.f) || !(descale_v > 0.f))
+    return FMHA_ERR_UNSUPPORTED;
+  if (d != fmha::Fp8Tile::D) return FMHA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FMHA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(N) + 256) * d * 2 >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+  const int64_t n_qt = (N + fmha::Fp8Tile::BM - 1) / fmha::Fp8Tile::BM;
+  const int64_t grid = static_cast<int64_t>(B) * H * n_qt;
+  if (grid >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
+  const uint64_t ib = static_cast<uint64_t>(B) * H * N * d;  // fp8 input bytes
+  const uint64_t ob = 2 * ib, lb = static_cast<uint64_t>(B) * H * N * 4;
+  if (overlap(o, ob, q, ib) || overlap(o, ob, k, ib) || overlap(o, ob, v, ib) ||
+      overlap(lse, lb, q, ib) || overlap(lse, lb, k, ib) || overlap(lse, lb, v, ib) ||
+      overlap(lse, lb, o, ob))
+    return FMHA_ERR_INVALID_ARGUMENT;
+
+  fmha::Fp8Params prm;
+  prm.q = static_cast<const uint8_t*>(q);
+  prm.k = static_cast<const uint8_t*>(k);
+  prm.v = static_cast<const uint8_t*>(v);
+  prm.o = static_cast<_Float16*>(o);
+  prm.lse = lse;
+  prm.N = N;
+  prm.n_qt = static_cast<int>(n_qt);
+  prm.total_wg = static_cast<int>(grid);
+  prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * descale_q * descale_k *
+                                      1.4426950408889634);
+  prm.descale_v = descale_v;
+  void* args[] = {&prm};
+  const void* fn = causal ? reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<true>)
+                          : reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<false>);
+  const hipError_t e = hipLaunchKernel(fn, dim3(prm.total_wg), dim3(fmha::Fp8Tile::THREADS), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
 
 extern "C" const char* fmha_status_str(int status) {

@@ -1,0 +1,451 @@
+// Fused multi-head attention forward pass with FP8 (OCP E4M3) Q, K and V, for
+// gfx950 (MI355X, CDNA4). Head dim 128.
+//
+// Tawa (CGO'26), section V-D, measures this variant on Hopper. Here both
+// products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, fp32
+// accumulate, unit block scales), at twice the FP16 MFMA rate:
+// - T stage, S^T = K Q^T: 2 key blocks x 2 k-steps of 64 bytes of d;
+// - C stage: the FP16 kernel's online softmax with lazy rescale, on fp32
+//   scores; the weights are rounded to E4M3 (p <= 2^RESCALE_LOG2 = 256 stays
+//   below E4M3's largest finite value, 448);
+// - U stage, O^T += V^T P^T: one MFMA per 32-row block of d per 64-key tile.
+// Row sums of the E4M3 weights run on v_mfma_scale_f32_16x16x128_f8f6f4 with
+// a 0/1 A operand, so O is normalised by exactly the weights that multiply V.
+//
+// Layouts. The MFMA pairs byte j of lane l in A with byte j of lane l in B;
+// lanes l and l + 32 carry two disjoint halves of the 64 k values. So:
+// - Q (B of S^T): lane l holds query l % 32, bytes d = 64 s + 32 (l / 32) ..
+//   +31 of k-step s, straight from the Q row;
+// - K (A of S^T): the same d bytes of key row key_of_row(l % 32) of the
+//   32-key block, two ds_read_b128;
+// - P^T (B of U): the fp32 score accumulator holds, in register i of
+//   block kb, key 32 kb + 16 (i / 8) + 8 (l / 32) + i % 8 of query l % 32
+//   (K rows are staged with bits 2 and 3 of the row swapped); byte
+//   j = 16 kb + i of the packed weights is that key;
+// - V^T (A of U): lane l needs d row l % 32 of the block and the same keys,
+//   i.e. runs of 8 consecutive keys, which ds_read_b64_tr_b8 returns from V
+//   in natural [key][d] layout: in each 16-lane group, source lane s reads 8
+//   bytes of row s / 2, and result lane i receives byte i of each of the 8
+//   rows.
+// K and V tiles arrive by LDS-DMA into 4-slot rings with XOR-swizzled 16-byte
+// chunks, so both kinds of read are free of bank conflicts.
+#pragma once
+
+#include "fmha_fwd_kernel.hpp"
+
+namespace fmha {
+
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx2 __attribute__((ext_vector_type(2)));
+
+struct Fp8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  _Float16* o;
+  float* lse;
+  int N;             // sequence length
+  int n_qt;          // query tiles per head
+  int total_wg;      // B * H * n_qt
+  float scale_log2;  // scale * descale_q * descale_k * log2(e)
+  float descale_v;
+};
+
+struct Fp8Tile {
+  static constexpr int D = 128;
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int QW = 32;                   // query rows per wave
+  static constexpr int BM = WAVES * QW;           // query rows per workgroup
+  static constexpr int BN = 64;                   // keys per pipeline stage
+  static constexpr int KB = BN / 32;              // 32-key blocks per stage
+  static constexpr int KSTEPS = D / 64;           // 64-byte k-steps of QK^T
+  static constexpr int DBLK = D / 32;             // 32-row blocks of O^T
+  static constexpr int RUNS = BN / 16;            // runs of 8 keys per V^T operand half
+  static constexpr int TILE_BYTES = BN * D;       // one K or V tile
+  static constexpr int SLOTS = 4;                 // ring depth for K and for V
+  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
+  static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / WAVES;  // per tile
+  static_assert(LOADS_PER_WAVE == 1, "one 16-byte DMA per lane per tile");
+};
+
+// 16-byte chunk swizzles (8 chunks per 128-byte row). K: 16 consecutive rows
+// read at one chunk hit distinct banks. V: 8 consecutive rows read at two
+// adjacent chunks (the transposing reads) hit distinct banks.
+__device__ __forceinline__ int fp8_k_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int fp8_v_swz(int row) { return 2 * ((row >> 1) & 3); }
+
+__device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Params p) {
+  using T = Fp8Tile;
+  constexpr int D = T::D;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) intx4 lds_intx4;
+  typedef __attribute__((address_space(3))) intx2 lds_intx2;
+  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
+  lds_char* const k_ring = (lds_char*)smem_raw;
+  lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;  // waves w and w + 4 share a SIMD
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // ---- work decomposition (as the FP16 kernel: one head's tiles per XCD) ----
+  const int G = p.total_wg;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int per = G >> 3, rem = G & 7;
+  const int t = xcd * per + min(xcd, rem) + (bid >> 3);
+  const int bh = t / p.n_qt;
+  int qt = t - bh * p.n_qt;
+  if (CAUSAL) qt = p.n_qt - 1 - qt;
+  const int q0 = qt * T::BM;
+  const int N = p.N;
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+
+  // ---- Q tile -> VGPRs: B operand of S^T = K Q^T ---------------------------
+  const int wave_q_lo = q0 + wave * T::QW;
+  const int qrow = wave_q_lo + l32;
+  intx8 qf[T::KSTEPS];
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s) {
+    const intx4 a = load16(rq, qrow * D + 64 * s + 32 * hh);
+    const intx4 b = load16(rq, qrow * D + 64 * s + 32 * hh + 16);
+    qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
+  floatx16 oacc[T::DBLK];
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
+  float m_run = -INFINITY;
+  // Row sums of the E4M3 weights: v_mfma_scale_f32_16x16x128_f8f6f4 with P^T
+  // (laid out for the 32x32x64 U MFMA) as B and E4M3 ones as A in lanes 0,
+  // 32 (queries 0..15) and 20, 52 (queries 16..31): register 0 of lane q < 32
+  // then holds query q's sum.
+  floatx4 lacc = {0.f, 0.f, 0.f, 0.f};
+  intx8 ones_a;
+  {
+    const int one = (lane == 0 || lane == 32 || lane == 20 || lane == 52) ? 0x38383838 : 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones_a[e] = one;
+  }
+
+  const int n_kv_all = (N + T::BN - 1) / T::BN;
+  const int n_kv = CAUSAL ? min(n_kv_all, (q0 + T::BM + T::BN - 1) / T::BN) : n_kv_all;
+  const int n_wave = CAUSAL ? min(n_kv, (wave_q_lo + T::QW - 1) / T::BN + 1) : n_kv;
+
+  // ---- producers: one 16-byte LDS-DMA per lane per tile ---------------------
+  // LDS chunk x = 64 * wave + lane of a tile; row r = x / 8 holds, for K, key
+  // key_of_row(r % 32) of its 32-row block.
+  int k_src, v_src;
+  {
+    const int x = 64 * wave + lane;
+    const int r = x >> 3, pos = x & 7;
+    k_src = ((r & ~31) | key_of_row(r & 31)) * D + 16 * (pos ^ fp8_k_swz(r));
+    v_src = r * D + 16 * (pos ^ fp8_v_swz(r));
+  }
+  auto fetch_k = [&](int j) __attribute__((always_inline)) {
+    load16_to_lds(rk, j * T::TILE_BYTES + k_src,
+                  k_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * 1024);
+  };
+  auto fetch_v = [&](int j) __attribute__((always_inline)) {
+    load16_to_lds(rv, j * T::TILE_BYTES + v_src,
+                  v_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * 1024);
+  };
+
+  // ---- consumer-side LDS offsets --------------------------------------------
+  // K (A of T): row l32 of block kb, chunks 4 s + 2 hh and + 1.
+  int k_rd[T::KSTEPS][2];
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_rd[s][e] = l32 * D + 16 * ((4 * s + 2 * hh + e) ^ fp8_k_swz(l32));
+  constexpr int K_BLOCK_BYTES = 32 * D;
+  // V^T (A of U), d block b: source lane s16 of 16-lane group g reads 8 bytes
+  // of key 16 rho + 8 hh + s16 / 2 at d = 32 b + 16 (g % 2) + 8 (s16 % 2);
+  // run rho adds 16 rows.
+  int v_rd[T::DBLK];
+  {
+    const int s16 = lane & 15, g = lane >> 4;
+    const int key = 8 * hh + (s16 >> 1);
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b)
+      v_rd[b] = key * D + 16 * ((2 * b + (g & 1)) ^ fp8_v_swz(key)) + 8 * (s16 & 1);
+  }
+  constexpr int V_RUN_BYTES = 16 * D;
+
+  floatx16 sacc[T::KB];  // S_j^T (fp32)
+  intx8 pf;              // P_j^T in E4M3: B operand of U_j
+
+  auto k_operand = [&](const lds_char* ks, int kb, int s) __attribute__((always_inline)) {
+    const intx4 a = *(const lds_intx4*)(ks + k_rd[s][0] + kb * K_BLOCK_BYTES);
+    const intx4 b = *(const lds_intx4*)(ks + k_rd[s][1] + kb * K_BLOCK_BYTES);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto v_operand = [&](const lds_char* vs, int b) __attribute__((always_inline)) {
+    intx2 r[T::RUNS];
+#pragma unroll
+    for (int rho = 0; rho < T::RUNS; ++rho)
+      r[rho] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2*)(vs + v_rd[b] + rho * V_RUN_BYTES));
+    return intx8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  };
+
+  const float c2 = p.scale_log2;
+
+  auto mask_tile = [&](int j) __attribute__((always_inline)) {
+    const int j0 = j * T::BN;
+    if ((j0 + T::BN > N) || (CAUSAL && j0 + T::BN - 1 > wave_q_lo)) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
+          if (key >= N || (CAUSAL && key > qrow)) sacc[kb][i] = -INFINITY;
+        }
+    }
+  };
+  // P_j^T in E4M3: byte j = 16 kb + i of pf is 2^(s c2 - m_run) of register i
+  // of block kb.
+  auto exp_pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, i = 4 * (w & 3);
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i + u], c2, -m_run));
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
+    }
+  };
+  auto tile_max = [&]() __attribute__((always_inline)) {
+    float t[11];
+#pragma unroll
+    for (int k = 0; k < 10; ++k) {
+      const int a = 3 * k;
+      t[k] = max3(sacc[a >> 4][a & 15], sacc[(a + 1) >> 4][(a + 1) & 15], sacc[(a + 2) >> 4][(a + 2) & 15]);
+    }
+    t[10] = max3(sacc[1][14], sacc[1][15], sacc[1][15]);
+    const float u0 = max3(t[0], t[1], t[2]), u1 = max3(t[3], t[4], t[5]);
+    const float u2 = max3(t[6], t[7], t[8]), u3 = max3(t[9], t[10], t[10]);
+    const float mx = max3(max3(u0, u1, u2), u3, u3);
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1])) * c2;
+  };
+  // C stage for key tile j: weights against the current reference, the row
+  // max alongside; the reference moves (and O, l are rescaled and the
+  // weights formed again) only when a row's max grows by more than
+  // 2^RESCALE_LOG2, so every weight stays <= 256.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    exp_pack();
+    asm volatile("" : "+v"(pf));
+    const float m_tile = tile_max();
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      lacc *= alpha;
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b) oacc[b] *= alpha;
+      exp_pack();
+    }
+  };
+  // T stage alone (tile 0): S^T = K_0 Q^T.
+  auto qk = [&]() __attribute__((always_inline)) {
+    const lds_char* ks = k_ring;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      sacc[kb] = mfma_fp8(k_operand(ks, kb, 0), qf[0], floatx16{});
+      sacc[kb] = mfma_fp8(k_operand(ks, kb, 1), qf[1], sacc[kb]);
+    }
+  };
+  // U stage alone (last tile of a wave).
+  auto pv = [&](int j) __attribute__((always_inline)) {
+    const lds_char* vs = v_ring + (j % T::SLOTS) * T::TILE_BYTES;
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b) oacc[b] = mfma_fp8(v_operand(vs, b), pf, oacc[b]);
+    lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones_a, pf, lacc, 0, 0, 0, 127, 0, 127);
+  };
+  // Matrix-core interval of iteration j: U_{j-1} and T_j alternating, then
+  // the row sum of P_{j-1}. Each operand is read AHEAD MFMAs before its use.
+  // The reads are inline asm: the compiler would otherwise wait for every
+  // LDS-DMA in flight (vmcnt(0)) before them, though none targets the slots
+  // read here. Their completion is waited for explicitly: LDS reads finish in
+  // order, so before MFMA i only the reads of operands i+1 .. i+AHEAD may be
+  // outstanding.
+  auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
+    constexpr int PREV = (U + T::SLOTS - 1) % T::SLOTS;
+    constexpr int NPV = T::DBLK, NT = T::KB * T::KSTEPS;
+    static_assert(NPV == NT, "U and T MFMAs alternate");
+    constexpr int NM = NPV + NT, AHEAD = 2;
+    constexpr int K_OFF = U * T::TILE_BYTES;
+    constexpr int V_OFF = T::SLOTS * T::TILE_BYTES + PREV * T::TILE_BYTES;
+    const uint32_t base = (uint32_t)(uintptr_t)k_ring;
+    auto reads = [](int i) constexpr { return (i & 1) == 0 ? T::RUNS : 2; };
+    auto operand = [&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_tag)::value;
+      constexpr int n = i >> 1;
+      intx8 r;
+      if constexpr ((i & 1) == 0) {
+        intx2 x[T::RUNS];
+#pragma unroll
+        for (int rho = 0; rho < T::RUNS; ++rho)
+          asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2"
+                       : "=v"(x[rho])
+                       : "v"(base + v_rd[n]), "i"(V_OFF + rho * V_RUN_BYTES));
+        r = intx8{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
+      } else {
+        constexpr int kb = n >> 1, st = n & 1;
+        intx4 a, b;
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(a) : "v"(base + k_rd[st][0]), "i"(K_OFF + kb * K_BLOCK_BYTES));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(b) : "v"(base + k_rd[st][1]), "i"(K_OFF + kb * K_BLOCK_BYTES));
+        r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      return r;
+    };
+    intx8 ring[AHEAD];
+    ring[0] = operand(std::integral_constant<int, 0>{});
+    ring[1] = operand(std::integral_constant<int, 1>{});
+    auto step = [&](auto i_tag) __attribute__((always_inline)) {
+      constexpr int i = decltype(i_tag)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      intx8 a = ring[i % AHEAD];
+      if constexpr (i + AHEAD < NM) ring[i % AHEAD] = operand(std::integral_constant<int, i + AHEAD>{});
+      constexpr int after = (i + 1 < NM ? reads(i + 1) : 0) + (i + 2 < NM ? reads(i + 2) : 0);
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(after));
+      constexpr int n = i >> 1;
+      // the empty asm keeps each MFMA in this interval (LLVM would sink the
+      // U MFMAs, whose results are not needed until the next interval)
+      if constexpr ((i & 1) == 0) {
+        oacc[n] = mfma_fp8(a, pf, oacc[n]);
+        asm volatile("" : "+v"(oacc[n]));
+      } else {
+        constexpr int kb = n >> 1, st = n & 1;
+        sacc[kb] = mfma_fp8(a, qf[st], st == 0 ? floatx16{} : sacc[kb]);
+        asm volatile("" : "+v"(sacc[kb]));
+      }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
+    static_assert(NM == 8, "eight MFMAs per interval");
+    lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones_a, pf, lacc, 0, 0, 0, 127, 0, 127);
+    asm volatile("" : "+v"(lacc));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- ping-pong schedule (as the FP16 kernel) ------------------------------
+  // Rings (slot = tile % 4). K_t: DMA issued in local interval 2t-5, waited
+  // for at the end of local 2t-2, read in global 2t .. 2t+1. V_t: DMA issued
+  // in local 2t-3, waited for at the end of local 2t, read in global 2t+2 ..
+  // 2t+3. The next DMA into either slot is issued at local 2t+3 or later.
+  auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+  auto mfma_sync = [&]() __attribute__((always_inline)) {
+    // everything but the two DMAs of the latest vector interval has landed
+    asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+  };
+  auto vector_sync = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto produce_issue = [&](int j) __attribute__((always_inline)) {
+    fetch_k(j + 3);
+    fetch_v(j + 2);
+  };
+  auto steady = [&](int j, auto u_tag) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_interval(u_tag);
+    __builtin_amdgcn_s_setprio(0);
+    mfma_sync();
+    produce_issue(j);
+    softmax(j);
+    vector_sync();
+  };
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
+
+  fetch_k(0);
+  fetch_k(1);
+  fetch_k(2);
+  fetch_v(0);
+  fetch_v(1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (group == 1) sync();
+
+  // j = 0: T_0, then C_0
+  if (n_wave > 0) qk();
+  mfma_sync();
+  produce_issue(0);
+  if (n_wave > 0) softmax(0);
+  vector_sync();
+  int j = 1;
+  for (; j + 4 <= n_wave; j += 4) {
+    steady(j, U1{});
+    steady(j + 1, U2{});
+    steady(j + 2, U3{});
+    steady(j + 3, U0{});
+  }
+  if (j < n_wave) {
+    steady(j, U1{});
+    ++j;
+    if (j < n_wave) {
+      steady(j, U2{});
+      ++j;
+      if (j < n_wave) {
+        steady(j, U3{});
+        ++j;
+      }
+    }
+  }
+  // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
+  // which the wave still loads its share of the workgroup's tiles
+  for (; j <= n_kv; ++j) {
+    if (j == n_wave && j >= 1) pv(j - 1);
+    mfma_sync();
+    produce_issue(j);
+    vector_sync();
+  }
+  if (group == 0) sync();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: O = descale_v O_acc / l, lse = (m + log2 l) ln 2 ---------------
+  // register i of block b holds d = 32 b + 8 (i / 4) + 4 hh + i % 4
+  const float l_tot = sum_halves(lacc[0]);
+  const float f = p.descale_v / l_tot;
+  if (qrow < N) {
+    _Float16* orow = p.o + head + (size_t)qrow * D;
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        half4 w = {(_Float16)(oacc[b][4 * g + 0] * f), (_Float16)(oacc[b][4 * g + 1] * f),
+                   (_Float16)(oacc[b][4 * g + 2] * f), (_Float16)(oacc[b][4 * g + 3] * f)};
+        *reinterpret_cast<half4*>(orow + 32 * b + 8 * g + 4 * hh) = w;
+      }
+    if (hh == 0)
+      p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace fmha

@@ -18,8 +18,8 @@ FMHA_ERR_INVALID_ARGUMENT = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_HIP = 3
 
-EXPORTS = ("fmha_fwd", "fmha_bwd", "fmha_bwd_workspace_bytes", "fmha_status_str",
-           "fmha_query_tile", "fmha_key_tile")
+EXPORTS = ("fmha_fwd", "fmha_fwd_fp8", "fmha_bwd", "fmha_bwd_workspace_bytes",
+           "fmha_status_str", "fmha_query_tile", "fmha_key_tile")
 
 
 class FmhaError(RuntimeError):
@@ -39,6 +39,9 @@ def lib():
         l.fmha_fwd.restype = ctypes.c_int
         l.fmha_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float,
                                                                             ctypes.c_void_p]
+        l.fmha_fwd_fp8.restype = ctypes.c_int
+        l.fmha_fwd_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] * 3 + [
+            ctypes.c_void_p] * 2 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_void_p]
         l.fmha_bwd.restype = ctypes.c_int
         l.fmha_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float,
                                                                              ctypes.c_void_p]
@@ -62,6 +65,12 @@ def fmha_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
     """The C entry point, pointers as integers. Returns the status code."""
     return lib().fmha_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), int(causal),
                           float(scale), stream)
+
+
+def fmha_fwd_fp8(q, k, v, dq, dk, dv, o, lse, B, H, N, d, causal, scale, stream) -> int:
+    """The C entry point, pointers as integers. Returns the status code."""
+    return lib().fmha_fwd_fp8(q, k, v, float(dq), float(dk), float(dv), o, lse, int(B), int(H),
+                              int(N), int(d), int(causal), float(scale), stream)
 
 
 def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, causal, scale, stream) -> int:
@@ -119,6 +128,44 @@ def forward(q, k, v, *, causal: bool = False, scale: float | None = None, out=No
     with torch.cuda.device(q.device):
         st = fmha_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, H, N, d, causal, scale, handle)
+    if st != FMHA_OK:
+        raise FmhaError(st)
+    return out, lse
+
+
+def forward_fp8(q8, k8, v8, descales, *, causal: bool = False, scale: float | None = None,
+                out=None, lse=None, stream=None):
+    """Attention forward with FP8 inputs: q8, k8, v8 are uint8 (or
+    float8_e4m3fn) contiguous [B, H, N, 128] torch tensors of OCP E4M3 bytes
+    on one GPU, descales = (dq, dk, dv). Returns (o fp16, lse fp32).
+    Launches on `stream` (default: torch's current stream) and does not
+    synchronise."""
+    import torch
+
+    ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    for t in (q8, k8, v8):
+        if t.dtype not in ok or t.dim() != 4 or t.shape != q8.shape:
+            raise ValueError("q8, k8, v8 must be uint8 / float8_e4m3fn tensors of one shape")
+        if not t.is_contiguous() or not t.is_cuda or t.device != q8.device:
+            raise ValueError("q8, k8, v8 must be contiguous and on one GPU")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if out.shape != q8.shape or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q8")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dq, dk, dv = (float(x) for x in descales)
+    with torch.cuda.device(q8.device):
+        st = fmha_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), dq, dk, dv, out.data_ptr(),
+                          lse.data_ptr(), B, H, N, d, causal, scale, handle)
     if st != FMHA_OK:
         raise FmhaError(st)
     return out, lse

@@ -111,3 +111,37 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(fmha, "_LIB_PATH", "/nonexistent/libfmha.so")
     with pytest.raises(RuntimeError, match="not built"):
         fmha.lib()
+
+
+def call_fp8(q=A, k=2 * A, v=3 * A, dq=0.01, dk=0.01, dv=0.01, o=4 * A, lse=5 * A, B=1, H=1,
+             N=128, d=128, causal=0, scale=0.088):
+    return fmha.fmha_fwd_fp8(q, k, v, dq, dk, dv, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fp8_null_pointer_is_invalid(which):
+    assert call_fp8(**{which: 0}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("which", ["dq", "dk", "dv", "scale"])
+def test_fp8_non_finite_factor_is_invalid(which):
+    assert call_fp8(**{which: math.nan}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("which", ["dq", "dk", "dv", "scale"])
+def test_fp8_non_positive_factor_is_unsupported(which):
+    assert call_fp8(**{which: 0.0}) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [64, 96, 256])
+def test_fp8_head_dim_other_than_128_is_unsupported(d):
+    assert call_fp8(d=d) == fmha.FMHA_ERR_UNSUPPORTED
+
+
+def test_fp8_output_aliasing_input_is_invalid():
+    assert call_fp8(q=4 * A) == fmha.FMHA_ERR_INVALID_ARGUMENT
+    assert call_fp8(lse=4 * A + 64) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+def test_fp8_empty_problem_is_ok():
+    assert call_fp8(B=0) == fmha.FMHA_OK

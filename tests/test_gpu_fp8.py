@@ -1,0 +1,137 @@
+"""Parity of the FP8 forward path (fmha_fwd_fp8, through the C ABI) with the
+CPU oracle on the same E4M3 bytes and descales.
+
+Bar, per output element (the oracle is fp64 on the decoded inputs):
+    |O - O_ref|     <= 7 rss_o + E sc_o + 2^-10 |O_ref| + 2^-16
+    |lse - lse_ref| <= 7 rss_l + E sc_l + 2^-20 |lse_ref| + 2^-16,  E = 2^-11.
+Two error sources, both reported per element by the oracle:
+- each softmax weight is rounded to E4M3: relative error <= 2^-4 in the
+  normal range, absolute <= 2^-10 of the largest weight below it (the
+  kernel's weights are <= 256 with the largest >= 1), independent from weight
+  to weight. To first order O moves by sum_j e_j (v_j - O) and lse by
+  sum_j e_j with e_j = max(2^-4 P_ij, 2^-10 max_j P_ij); the oracle's
+  rss_o = sqrt(sum_j e_j^2 (v_j - O)^2), rss_l = sqrt(sum_j e_j^2), and by
+  Hoeffding's bound 7 rss is exceeded with probability below 1e-10;
+- the FP8 MFMA does not add its products exactly: on random E4M3 operands
+  its error reached 2^-11.9 of the sum of the products' magnitudes (a probe
+  of v_mfma_scale_f32_32x32x64_f8f6f4 against exact sums). A score error
+  |ds_ij| <= E a_ij, a_ij = scale sum_c |q_ic k_jc|, moves O by at most
+  E sum_j P_ij a_ij |v_j - O| = E sc_o and lse by at most E sc_l; it is not
+  taken as random.
+2^-10 |O_ref| covers the fp16 rounding of O; the floors cover fp32 sums.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from software_pipelining_fmha_amd import fmha, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def run(b, sc, causal, scale):
+    import torch
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0") for x in b)
+    B, H, N, d = b[0].shape
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.float16, device="cuda:0")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    fmha.forward_fp8(tq, tk, tv, sc, causal=causal, scale=float(scale), out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+E_MFMA = 2.0 ** -11
+
+
+def check(o, lse, rows, ref, label):
+    o_ref, l_ref, ro, rl, so, sl = ref
+    b, h, i = rows[:, 0], rows[:, 1], rows[:, 2]
+    og, lg = o[b, h, i].astype(np.float64), lse[b, h, i].astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), label + ": non-finite output"
+    eo, el = np.abs(og - o_ref), np.abs(lg - l_ref)
+    to = 7 * ro + E_MFMA * so + 2.0 ** -10 * np.abs(o_ref) + 2.0 ** -16
+    tl = 7 * rl + E_MFMA * sl + 2.0 ** -20 * np.abs(l_ref) + 2.0 ** -16
+    print("%s: rows=%d max|dO|=%.3e (err/bar %.3f) max|dlse|=%.3e (err/bar %.3f)" % (
+        label, len(rows), eo.max(), (eo / to).max(), el.max(), (el / tl).max()), flush=True)
+    assert (eo <= to).all(), "%s: O error above the bar" % label
+    assert (el <= tl).all(), "%s: lse error above the bar" % label
+
+
+SMALL = [(2, 2, n, c) for n in (1, 2, 63, 64, 65, 127, 128, 200, 256, 257, 333, 600)
+         for c in (False, True)]
+
+
+@pytest.mark.parametrize("B,H,N,causal", SMALL)
+def test_small_and_ragged_shapes_every_row(B, H, N, causal, device):
+    print("fp8 small B=%d H=%d N=%d causal=%d" % (B, H, N, causal), flush=True)
+    b, sc = inputs.draw_qkv_fp8(B, H, N, 128, seed=6000 + 3 * N + causal)
+    scale = np.float32(1 / math.sqrt(128))
+    o, lse = run(b, sc, causal, scale)
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 small")
+
+
+@pytest.mark.parametrize("idx", range(len(inputs.FP8_WORKLOADS)),
+                         ids=[w.name for w in inputs.FP8_WORKLOADS])
+def test_fp8_workload_parity(idx, device):
+    w = inputs.FP8_WORKLOADS[idx]
+    print("fp8 workload %s" % w.name, flush=True)
+    b, sc, scale = inputs.fp8_workload_inputs(idx)
+    o, lse = run(b, sc, w.causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten or NaN output"
+    rows = inputs.fp8_workload_rows(idx)
+    if w.sampled_rows == 0 and w.B * w.H > 4:
+        rows = rows[np.isin(rows[:, 0] * w.H + rows[:, 1], [0, 37, 77, 127])]
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=w.causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, w.name)
+
+
+def test_fp8_uniform_keys_every_row(device):
+    """All key rows equal: O_i is the mean of the visible value rows (in the
+    descaled values) and lse_i = scale * q_i . u + ln|J_i|. Every score of a
+    row carries the same MFMA error, so every weight is exactly 1 in E4M3: O
+    is exact up to fp32 sums and its fp16 rounding, and lse moves by that one
+    score error, at most E scale sum_c |q_ic u_c|."""
+    B, H, N, d = 2, 4, 1000, 128
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6161)
+    q8, k8, v8 = (np.array(x) for x in b)
+    k8[:] = k8[:, :, :1]
+    o, lse = run((q8, k8, v8), sc, True, np.float32(1 / math.sqrt(d)))
+    q, u, v = (oracle.e4m3_to_double(x) * float(s) for x, s in zip((q8, k8[:, :, :1], v8), sc))
+    cnt = np.arange(1, N + 1, dtype=np.float64)
+    mean = np.cumsum(v, axis=2) / cnt[None, None, :, None]
+    s_ = float(np.float32(1 / math.sqrt(d))) * np.einsum("bhnd,bhd->bhn", q, u[:, :, 0])
+    assert np.abs(o - mean).max() <= 2.0 ** -10 * np.abs(mean).max() + 1e-4
+    a = float(np.float32(1 / math.sqrt(d))) * np.einsum("bhnd,bhd->bhn", np.abs(q), np.abs(u[:, :, 0]))
+    err = np.abs(lse - (s_ + np.log(cnt)))
+    print("uniform keys: max |dlse| = %.3e, err/bar %.3f" % (err.max(), (err / (E_MFMA * a + 1e-5)).max()),
+          flush=True)
+    assert (err <= E_MFMA * a + 1e-5).all()
+
+
+def test_fp8_deterministic_bitwise(device):
+    b, sc = inputs.draw_qkv_fp8(2, 4, 700, 128, seed=6262)
+    a1 = run(b, sc, False, np.float32(0.088388))
+    a2 = run(b, sc, False, np.float32(0.088388))
+    assert np.array_equal(a1[0].view(np.uint16), a2[0].view(np.uint16))
+    assert np.array_equal(a1[1].view(np.uint32), a2[1].view(np.uint32))
+
+
+def test_fp8_guard_bands_untouched(device):
+    import torch
+    B, H, N, d = 1, 2, 333, 128
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6363)
+    tq, tk, tv = (torch.from_numpy(x).to("cuda:0") for x in b)
+    pad, n = 4096, B * H * N * d
+    ob = torch.full((n + 2 * pad,), 77.0, dtype=torch.float16, device="cuda:0")
+    lb = torch.full((B * H * N + 2 * pad,), -9.0, dtype=torch.float32, device="cuda:0")
+    fmha.forward_fp8(tq, tk, tv, sc, causal=True, out=ob[pad:pad + n].view(B, H, N, d),
+                     lse=lb[pad:pad + B * H * N].view(B, H, N))
+    torch.cuda.synchronize()
+    o, l = ob.cpu().numpy(), lb.cpu().numpy()
+    assert (o[:pad] == np.float16(77.0)).all() and (o[-pad:] == np.float16(77.0)).all()
+    assert (l[:pad] == -9.0).all() and (l[-pad:] == -9.0).all()
+    assert np.isfinite(o[pad:-pad]).all() and np.isfinite(l[pad:-pad]).all()

@@ -57,13 +57,16 @@ def test_matches_fp16_oracle_on_exact_inputs(causal, descales):
 @pytest.mark.parametrize("causal", [False, True])
 def test_tolerance_scales_match_definition(causal):
     """rss_o[c] = sqrt(sum_j e_j^2 (v_jc - o_c)^2), rss_l = sqrt(sum_j e_j^2),
-    e_j = max(2^-4 P_ij, 2^-10 max_j P_ij), with P from scipy's softmax."""
+    e_j = max(2^-4 P_ij, 2^-10 max_j P_ij); sc_o[c] = sum_j P_ij a_ij |v_jc - o_c|,
+    sc_l = sum_j P_ij a_ij, a_ij = scale sum_c |q_ic k_jc|; P from scipy's
+    softmax."""
     from scipy.special import softmax
     B, H, N, d = 1, 1, 21, 8
     q8, k8, v8 = (random_e4m3((B, H, N, d), s) for s in (4, 5, 6))
     ds = (0.5, 0.25, 2.0)
     scale = np.float32(0.7)
-    o, lse, ro, rl = oracle.fmha_fp8_all(q8, k8, v8, ds, causal=causal, scale=scale, rss=True)
+    o, lse, ro, rl, so, sl = oracle.fmha_fp8_all(q8, k8, v8, ds, causal=causal, scale=scale,
+                                                 rss=True)
     q, k, v = (oracle.e4m3_to_double(x)[0, 0] * s for x, s in zip((q8, k8, v8), ds))
     s_ = float(scale) * q @ k.T
     if causal:
@@ -71,8 +74,13 @@ def test_tolerance_scales_match_definition(causal):
     P = softmax(s_, axis=1)
     e = np.maximum(P / 16, P.max(axis=1, keepdims=True) / 1024) * (P > 0)
     np.testing.assert_allclose(rl[0, 0], np.sqrt((e ** 2).sum(1)), rtol=1e-12)
-    ref = np.sqrt(np.einsum("ij,ijc->ic", e ** 2, (v[None, :, :] - o[0, 0][:, None, :]) ** 2))
+    dev = np.abs(v[None, :, :] - o[0, 0][:, None, :])
+    ref = np.sqrt(np.einsum("ij,ijc->ic", e ** 2, dev ** 2))
     np.testing.assert_allclose(ro[0, 0], ref, rtol=1e-12, atol=1e-300)
+    a = float(scale) * np.einsum("ic,jc->ij", np.abs(q), np.abs(k))
+    Pz = np.where(np.isfinite(s_), P, 0.0)
+    np.testing.assert_allclose(sl[0, 0], (Pz * a).sum(1), rtol=1e-12)
+    np.testing.assert_allclose(so[0, 0], np.einsum("ij,ijc->ic", Pz * a, dev), rtol=1e-12, atol=1e-300)
 
 
 def test_quantizer_round_trip():
