@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,28 +54,31 @@ FP8_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_fp8_kernel.hpp",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fmha_fwd_b4h32n16384d128.txt")
 
 
-def kernel_digest() -> str:
+_COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
+
+
+def _source_digest(paths) -> str:
+    """Digest of the code in `paths` with comments and whitespace removed, so
+    that a profile stays matched to its kernel across comment-only edits."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            code = _COMMENT.sub(" ", f.read())
+        h.update(" ".join(code.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
+
+
+def kernel_digest() -> str:
+    return _source_digest(KERNEL_SOURCES)
 
 
 def fp8_digest() -> str:
-    h = hashlib.sha256()
-    for rel in FP8_SOURCES + KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _source_digest(FP8_SOURCES + KERNEL_SOURCES)
 
 
 def bwd_digest() -> str:
-    h = hashlib.sha256()
-    for rel in BWD_SOURCES + KERNEL_SOURCES[1:]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _source_digest(BWD_SOURCES + KERNEL_SOURCES[1:])
 
 
 def recorded_traffic(workload: str):

@@ -3,6 +3,7 @@
 // the error contract are stated in include/fmha.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -15,6 +16,24 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Compute units of the current device, rounded down to a multiple of 8 (one
+// workgroup per CU for the persistent forward kernel; 8 XCDs). Cached per
+// device; 0 if the query fails.
+int persistent_grid() {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const int g = cus & ~7;
+  if (dev >= 0 && dev < 64 && g > 0) cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
 bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -24,8 +43,13 @@ template <int D, bool CAUSAL>
 int launch(const fmha::Params& prm, hipStream_t stream) {
   using T = fmha::Tile<D>;
   void* args[] = {const_cast<fmha::Params*>(&prm)};
+  // persistent: every tile if they fit in one wave of workgroups, else one
+  // workgroup per CU (a multiple of 8), each walking several tiles
+  const int cap = persistent_grid();
+  if (cap <= 0) return FMHA_ERR_HIP;
+  const int grid = prm.total_wg < cap ? prm.total_wg : cap;
   const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_fwd_kernel<D, CAUSAL>),
-                                       dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+                                       dim3(grid), dim3(T::THREADS), args, 0, stream);
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
 
@@ -214,7 +238,10 @@ extern "C" int fmha_fwd_fp8(const void* q, const void* k, const void* v, float d
   void* args[] = {&prm};
   const void* fn = causal ? reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<true>)
                           : reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<false>);
-  const hipError_t e = hipLaunchKernel(fn, dim3(prm.total_wg), dim3(fmha::Fp8Tile::THREADS), args, 0,
+  const int cap = persistent_grid();
+  if (cap <= 0) return FMHA_ERR_HIP;
+  const int wgs = prm.total_wg < cap ? prm.total_wg : cap;
+  const hipError_t e = hipLaunchKernel(fn, dim3(wgs), dim3(fmha::Fp8Tile::THREADS), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }

@@ -80,13 +80,12 @@ __device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Params p) {
+__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw) {
   using T = Fp8Tile;
   constexpr int D = T::D;
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) intx4 lds_intx4;
   typedef __attribute__((address_space(3))) intx2 lds_intx2;
-  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
 
@@ -97,12 +96,6 @@ __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Pa
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- work decomposition (as the FP16 kernel: one head's tiles per XCD) ----
-  const int G = p.total_wg;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int per = G >> 3, rem = G & 7;
-  const int t = xcd * per + min(xcd, rem) + (bid >> 3);
   const int bh = t / p.n_qt;
   int qt = t - bh * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;
@@ -445,6 +438,21 @@ __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Pa
       }
     if (hh == 0)
       p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+// Persistent, with the FP16 kernel's tile schedule: one workgroup per CU (a
+// multiple of 8) or one per tile, odd passes reversed within each XCD.
+template <bool CAUSAL>
+__global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Params p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Fp8Tile::LDS_BYTES];
+  const int G = p.total_wg;
+  const int per = G >> 3, rem = G & 7;
+  const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
+  for (int r = 0; r * (int)gridDim.x < G; ++r) {
+    const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
+    if (tile >= G) break;
+    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw);
   }
 }
 

@@ -1,7 +1,7 @@
 // Fused multi-head attention forward pass for gfx950 (MI355X, CDNA4).
 //
-// One workgroup owns one (batch, head, query tile). The query tile stays in
-// VGPRs for the whole kernel. Key/value tiles stream from HBM into LDS rings
+// The kernel is persistent: one workgroup per CU walks the (batch, head,
+// query tile) tiles, one at a time. Per tile the query rows stay in VGPRs. Key/value tiles stream from HBM into LDS rings
 // by LDS-DMA. Each stage of the pages maps onto gfx950 units:
 // - T stage, S = Q K^T (Tawa, section III-D): fp16 MFMA, fp32 accumulate;
 // - C stage, online softmax with rescale (PipeThreader's softmax and
@@ -152,12 +152,10 @@ __device__ __forceinline__ int k_chunk_off(int p, int c) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p) {
+__device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw) {
   using T = Tile<D>;
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) half8 lds_half8;
-  // LDS: 3-slot rings of K tiles, of V^T tiles and of V tiles (natural layout).
-  __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
   lds_char* const v_stage = v_ring + T::SLOTS * T::VT_BYTES;
@@ -170,14 +168,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   const int hh = lane >> 5;
 
   // ---- work decomposition -------------------------------------------------
-  // Workgroups go round-robin over the 8 XCDs (bid % 8). Renumber them so
-  // that consecutive tile ids, i.e. the query tiles of one head, run on one
-  // XCD and share its L2 copy of that head's K and V.
-  const int G = p.total_wg;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int per = G >> 3, rem = G & 7;
-  const int t = xcd * per + min(xcd, rem) + (bid >> 3);
+  // Tile id t -> (b*H + h, query tile). The persistent loop below hands one
+  // XCD consecutive ids, i.e. the query tiles of one head, so they share its
+  // L2 copy of that head's K and V.
   const int bh = t / p.n_qt;
   int qt = t - bh * p.n_qt;
   if (CAUSAL) qt = p.n_qt - 1 - qt;  // heaviest query tiles of a head first
@@ -622,6 +615,28 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
       }
     if (hh == 0)
       p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Tile<D>::LDS_BYTES];
+  const int G = p.total_wg;
+  const int per = G >> 3, rem = G & 7;
+  // Persistent schedule (Tawa, sections IV-B and V-E: launch as many
+  // workgroups as the chip holds and let them iterate over tiles). Workgroup
+  // b runs on XCD b % 8; the grid is either every tile (one each) or a
+  // multiple of 8 no larger than the CU count. Pass r hands out tiles
+  // r * grid .. r * grid + grid - 1, walking the workgroups of each XCD in
+  // reverse on odd passes, so that a workgroup that drew a heavy causal tile
+  // draws a light one next. Tile ids map to (b, h, query tile) so that one
+  // XCD's tiles are consecutive ids (one head's query tiles share its L2).
+  const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
+  for (int r = 0; r * (int)gridDim.x < G; ++r) {
+    const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
+    if (tile >= G) break;
+    const int t = x * per + min(x, rem) + (tile >> 3);
+    fwd_tile<D, CAUSAL>(p, t, smem_raw);
   }
 }
 

@@ -89,6 +89,33 @@ def test_fp8_workload_parity(idx, device):
     check(o, lse, rows, ref, w.name)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_persistent_passes_cover_every_tile(causal, device):
+    """More query tiles than compute units, not a multiple of 8: several
+    passes per workgroup with a partial last one. Every output is written
+    and rows at both edges of every tile match the oracle."""
+    import torch
+    B, H, N, d = 3, 31, 1000, 128
+    bm = 256
+    tiles = B * H * (-(-N // bm))
+    assert tiles > torch.cuda.get_device_properties(0).multi_processor_count and tiles % 8
+    print("fp8 persistent cover causal=%d tiles=%d" % (causal, tiles), flush=True)
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6400 + causal)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(b, sc, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rng = np.random.default_rng(causal)
+    rows = []
+    for bb in range(B):
+        for h in range(H):
+            for t0 in range(0, N, bm):
+                t1 = min(t0 + bm, N) - 1
+                rows += [(bb, h, t0), (bb, h, t1), (bb, h, int(rng.integers(t0, t1 + 1)))]
+    rows = np.array(rows, dtype=np.int64)
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 persistent cover")
+
+
 def test_fp8_uniform_keys_every_row(device):
     """All key rows equal: O_i is the mean of the visible value rows (in the
     descaled values) and lse_i = scale * q_i . u + ln|J_i|. Every score of a

@@ -177,6 +177,40 @@ def test_one_hot_scores_select_one_value_row(d, device):
     assert np.abs(lse - 4096 * float(scale)).max() <= TOL_LSE
 
 
+def tile_edge_rows(B, H, N, bm, seed):
+    """Per (b, h, query tile): its first row, its last row and one row
+    between them."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, N, bm):
+                t1 = min(t0 + bm, N) - 1
+                out += [(b, h, t0), (b, h, t1), (b, h, int(rng.integers(t0, t1 + 1)))]
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
+def test_persistent_passes_cover_every_tile(d, causal, device):
+    """More query tiles than compute units, and a count that is not a
+    multiple of 8: workgroups walk several tiles each, odd passes in
+    reverse, and the last pass is partial. Every output is written (the NaN
+    fill is gone), and rows at both edges of every tile match the oracle."""
+    torch = torch_mod()
+    B, H, N = 3, 31, 1000
+    bm = fmha.fmha_query_tile(d)
+    tiles = B * H * (-(-N // bm))
+    assert tiles > torch.cuda.get_device_properties(0).multi_processor_count and tiles % 8
+    print("persistent cover d=%d causal=%d tiles=%d" % (d, causal, tiles), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=1700 + d + causal)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rows = tile_edge_rows(B, H, N, bm, seed=d + causal)
+    o_ref, lse_ref = oracle.fmha_rows(q, k, v, rows, causal=causal, scale=scale)
+    check_rows(o, lse, rows, o_ref, lse_ref, "persistent cover")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_first_row_is_first_value_row(d, device):
     q, k, v = inputs.draw_qkv(2, 2, 257, d, seed=12)
