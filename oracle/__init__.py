@@ -4,7 +4,11 @@ TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench
 script's CPU-baseline leg may import this package. The HIP library and its
 Python binding never import it, and it imports nothing from them.
 
-`fmha_oracle.c` holds the arithmetic: the plain fp64 definition
+`gemm_oracle.c` holds the plain matrix product C = A x B in fp64 (the
+GEMM that the performance-model page for warp-specialised kernels tiles),
+pinned by `tests/test_oracle_gemm.py`.
+
+`fmha_oracle.c` holds the attention arithmetic: the plain fp64 definition
 softmax(scale * Q K^T) V, plus the natural-log logsumexp of each row, one
 query row at a time; and the gradients of sum(dO * O) with respect to Q, K
 and V, one row at a time, by the chain rule through that definition (the
@@ -27,16 +31,18 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fmha_oracle.c")
+_GEMM_SRC = os.path.join(_HERE, "gemm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile fmha_oracle.c with gcc into liboracle.so (next to the source)."""
+    """Compile fmha_oracle.c and gemm_oracle.c with gcc into liboracle.so
+    (next to the sources)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                        _SRC, "-o", tmp, "-lm"], check=True)
+                        _SRC, _GEMM_SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -72,6 +78,10 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_e4m3_to_double.restype = None
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        lib.oracle_gemm_rows.restype = ctypes.c_int
+        lib.oracle_gemm_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_half_to_double.restype = None
         lib.oracle_half_to_double.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int64]
@@ -224,3 +234,29 @@ def fmha_fp8_all(q8, k8, v8, descales, *, causal: bool, scale, threads: int | No
                         threads=threads, rss=rss)
     shapes = [(B, H, N, d), (B, H, N)] * 3
     return tuple(x.reshape(sh) for x, sh in zip(out, shapes))
+
+
+def gemm_rows(a, b, rows, *, threads: int | None = None, magnitude: bool = False):
+    """Rows of C = A x B in fp64. a: float16 [M, K], b: float16 [K, N], both
+    row-major; rows: int [n]. Returns c float64 [n, N], and with
+    magnitude=True also cabs = sum_k |A[m][k] B[k][n]| of the same shape."""
+    a, b = _as_half(a), _as_half(b)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("a must be [M, K] and b [K, N]")
+    M, K = a.shape
+    N = b.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    c = np.empty((rows.size, N), dtype=np.float64)
+    ca = np.empty_like(c) if magnitude else None
+    st = _load().oracle_gemm_rows(a.ctypes.data, b.ctypes.data, M, N, K, rows.ctypes.data,
+                                  rows.size, c.ctypes.data,
+                                  ca.ctypes.data if ca is not None else None,
+                                  int(threads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_gemm_rows failed with status %d" % st)
+    return (c, ca) if magnitude else c
+
+
+def gemm_all(a, b, *, threads: int | None = None, magnitude: bool = False):
+    """Every row of C = A x B (and of cabs with magnitude=True)."""
+    return gemm_rows(a, b, np.arange(a.shape[0]), threads=threads, magnitude=magnitude)
