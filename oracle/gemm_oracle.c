@@ -43,6 +43,16 @@ static double gemm_half(uint16_t h)
     return sign ? -v : v;
 }
 
+/* every binary16 value, widened once */
+static double g_gemm_half[65536];
+static pthread_once_t g_gemm_once = PTHREAD_ONCE_INIT;
+
+static void build_gemm_table(void)
+{
+    for (int h = 0; h < 65536; ++h)
+        g_gemm_half[h] = gemm_half((uint16_t)h);
+}
+
 typedef struct {
     const uint16_t *a, *b;
     int64_t M, N, K;
@@ -57,36 +67,35 @@ static void *gemm_worker(void *arg)
 {
     gemm_job_t *jb = (gemm_job_t *)arg;
     const int64_t N = jb->N, K = jb->K;
-    double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
-    if (!arow) {
-        jb->status = -2;
-        return NULL;
-    }
+    /* Per requested row m: for k = 0, 1, ..., K-1 add A[m][k] * B[k][n] into
+     * every column n. Each element's sum still runs over k in increasing
+     * order; walking B row by row only keeps the reads contiguous. */
     for (int64_t r = jb->first; r < jb->last; ++r) {
         const int64_t m = jb->rows[r];
-        for (int64_t k = 0; k < K; ++k)
-            arow[k] = gemm_half(jb->a[m * K + k]);
         double *c = jb->c + r * N, *ca = jb->cabs ? jb->cabs + r * N : NULL;
         for (int64_t n = 0; n < N; ++n) {
-            double s = 0.0, sa = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
-                const double p = arow[k] * gemm_half(jb->b[k * N + n]);
-                s += p;
-                sa += fabs(p);
-            }
-            c[n] = s;
+            c[n] = 0.0;
             if (ca)
-                ca[n] = sa;
+                ca[n] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            const double am = g_gemm_half[jb->a[m * K + k]];
+            const uint16_t *brow = jb->b + k * N;
+            for (int64_t n = 0; n < N; ++n) {
+                const double p = am * g_gemm_half[brow[n]];
+                c[n] += p;
+                if (ca)
+                    ca[n] += fabs(p);
+            }
         }
     }
-    free(arow);
     return NULL;
 }
 
 /*
  * oracle_gemm_rows: rows `rows[0..n_rows)` of C = A x B (and of Cabs, if
- * cabs is not NULL) into c[n_rows][N]. Returns 0, -1 for an argument error
- * (a row outside [0, M), a negative size) or -2 if memory ran out.
+ * cabs is not NULL) into c[n_rows][N]. Returns 0, or -1 for an argument
+ * error (a row outside [0, M), a negative size).
  */
 int oracle_gemm_rows(const uint16_t *a, const uint16_t *b, int64_t M, int64_t N, int64_t K,
                      const int64_t *rows, int64_t n_rows, double *c, double *cabs, int threads)
@@ -96,6 +105,7 @@ int oracle_gemm_rows(const uint16_t *a, const uint16_t *b, int64_t M, int64_t N,
     for (int64_t r = 0; r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= M)
             return -1;
+    pthread_once(&g_gemm_once, build_gemm_table);
     if (threads < 1)
         threads = 1;
     if (threads > 64)

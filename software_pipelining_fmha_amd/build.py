@@ -11,8 +11,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfmha.so")
-SOURCES = [os.path.join(CSRC, "fmha_api.hip")]
-HEADERS = [os.path.join(CSRC, "fmha_fwd_kernel.hpp"), os.path.join(ROOT, "include", "fmha.h")]
+SOURCES = [os.path.join(CSRC, "fmha_api.hip"), os.path.join(CSRC, "ws_gemm_api.hip")]
+HEADERS = [os.path.join(CSRC, "fmha_fwd_kernel.hpp"), os.path.join(CSRC, "ws_gemm_kernel.hpp"),
+           os.path.join(ROOT, "include", "fmha.h"), os.path.join(ROOT, "include", "ws_gemm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -24,14 +25,30 @@ FLAGS = [
 
 
 def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
+    """One hipcc line that compiles and links every source."""
     return [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *SOURCES, "-o", out]
 
 
 def build(extra: list[str] | None = None, out: str = LIB) -> str:
+    """Compile each source to an object in parallel, then link the library."""
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.run(command(tmp, extra), check=True)
-    os.replace(tmp, out)
+    objs = ["%s.%d.o" % (tmp, i) for i in range(len(SOURCES))]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = [subprocess.Popen([HIPCC, *compile_flags, *(extra or []), "-c", "-I",
+                               os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", obj])
+             for src, obj in zip(SOURCES, objs)]
+    codes = [p.wait() for p in procs]
+    try:
+        if any(codes):
+            raise subprocess.CalledProcessError(max(codes), "hipcc -c")
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                       check=True)
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

@@ -1,0 +1,244 @@
+// C ABI of the warp-specialised GEMM and of its analytic performance model.
+// The operations, limits and error contract are stated in include/ws_gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "ws_gemm.h"
+#include "ws_gemm_kernel.hpp"
+
+namespace {
+
+constexpr int OK = 0, INVALID = 1, UNSUPPORTED = 2, HIP_FAIL = 3;
+constexpr int SPIN_LIMIT = 1 << 22;
+
+struct Variant {
+  int tm, tn, tk, ring;
+};
+
+// Every (T_M, T_N, T_K, ring) whose ring fits the LDS and whose tile loads
+// fit the DMA wave's vmcnt range.
+#define WS_VARIANTS(X)                                                                        \
+  X(64, 64, 64, 1) X(64, 64, 64, 2) X(64, 64, 64, 3) X(64, 64, 64, 4) X(64, 64, 128, 1)       \
+  X(64, 64, 128, 2) X(64, 64, 128, 3) X(64, 64, 128, 4) X(64, 128, 64, 1) X(64, 128, 64, 2)   \
+  X(64, 128, 64, 3) X(64, 128, 64, 4) X(64, 128, 128, 1) X(64, 128, 128, 2)                  \
+  X(64, 128, 128, 3) X(128, 64, 64, 1) X(128, 64, 64, 2) X(128, 64, 64, 3)                   \
+  X(128, 64, 64, 4) X(128, 64, 128, 1) X(128, 64, 128, 2) X(128, 64, 128, 3)                 \
+  X(128, 128, 64, 1) X(128, 128, 64, 2) X(128, 128, 64, 3) X(128, 128, 64, 4)                \
+  X(128, 128, 128, 1) X(128, 128, 128, 2) X(256, 64, 64, 1) X(256, 64, 64, 2)                \
+  X(256, 64, 64, 3) X(256, 128, 64, 1) X(256, 128, 64, 2) X(256, 128, 64, 3)
+
+#define WS_ENTRY(TM, TN, TK, R) {TM, TN, TK, R},
+
+const Variant VARIANTS[] = {WS_VARIANTS(WS_ENTRY)};
+constexpr int N_VARIANTS = sizeof(VARIANTS) / sizeof(VARIANTS[0]);
+
+const Variant* find_variant(int tm, int tn, int tk, int ring) {
+  for (const Variant& v : VARIANTS)
+    if (v.tm == tm && v.tn == tn && v.tk == tk && v.ring == ring) return &v;
+  return nullptr;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_cus() {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cus > 0) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+template <int TM, int TN, int TK, int R>
+hipError_t launch_one(const wsgemm::GemmParams& prm, unsigned grid, hipStream_t stream) {
+  void* args[] = {const_cast<wsgemm::GemmParams*>(&prm)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&wsgemm::ws_gemm_kernel<TM, TN, TK, R>),
+                         dim3(grid), dim3(wsgemm::GemmTile<TM, TN, TK, R>::THREADS), args, 0,
+                         stream);
+}
+
+#define WS_CASE(TM, TN, TK, R) \
+  if (v.tm == TM && v.tn == TN && v.tk == TK && v.ring == R) return launch_one<TM, TN, TK, R>(prm, grid, stream);
+
+hipError_t launch_variant(const Variant& v, const wsgemm::GemmParams& prm, unsigned grid,
+                          hipStream_t stream) {
+  WS_VARIANTS(WS_CASE)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" int ws_gemm_config_count(void) { return N_VARIANTS; }
+
+extern "C" int ws_gemm_config(int idx, int* tile_m, int* tile_n, int* tile_k, int* ring) {
+  if (idx < 0 || idx >= N_VARIANTS) return 1;
+  const Variant& v = VARIANTS[idx];
+  if (tile_m) *tile_m = v.tm;
+  if (tile_n) *tile_n = v.tn;
+  if (tile_k) *tile_k = v.tk;
+  if (ring) *ring = v.ring;
+  return 0;
+}
+
+extern "C" size_t ws_gemm_trace_words(int M, int N, int K, int tile_m, int tile_n, int tile_k) {
+  if (M <= 0 || N <= 0 || K < 0 || tile_m <= 0 || tile_n <= 0 || tile_k <= 0) return 0;
+  const int64_t tiles = cdiv(M, tile_m) * cdiv(N, tile_n);
+  return (size_t)(tiles * (cdiv(K, tile_k) + 1) * wsgemm::TRACE_FIELDS);
+}
+
+extern "C" double ws_model_stage_times(int S, int ring, double t_load_a, double t_load_b,
+                                       double t_math, double* s_a, double* s_b, double* s_m,
+                                       double* math_wait) {
+  if (S < 0 || ring < 1) return -1.0;
+  if (math_wait) *math_wait = 0.0;
+  if (S == 0) return 0.0;
+  // start times of MATH stages, kept for the last `ring` stages
+  std::vector<double> sm_hist((size_t)ring, 0.0);
+  double prev_sb = 0.0, prev_sm = 0.0, wait = 0.0;
+  for (int i = 0; i < S; ++i) {
+    // MATH stage i - ring has released its slot at S_m(i - ring) + T_MATH
+    const bool slot_term = i >= ring;
+    const double slot_free = slot_term ? sm_hist[(size_t)(i % ring)] + t_math : 0.0;
+    double sa = 0.0;
+    if (i > 0) sa = prev_sb + t_load_b;
+    if (slot_term) sa = std::max(sa, slot_free);
+    double sb = sa + t_load_a;
+    if (slot_term) sb = std::max(sb, slot_free);
+    double sm = sb + t_load_b;
+    if (i > 0) sm = std::max(sm, prev_sm + t_math);
+    wait += (i == 0) ? sm : sm - (prev_sm + t_math);
+    if (s_a) s_a[i] = sa;
+    if (s_b) s_b[i] = sb;
+    if (s_m) s_m[i] = sm;
+    sm_hist[(size_t)(i % ring)] = sm;
+    prev_sb = sb;
+    prev_sm = sm;
+  }
+  if (math_wait) *math_wait = wait;
+  return prev_sm + t_math;
+}
+
+extern "C" double ws_model_launch_time(const ws_model_params* p, int M, int N, int K, int tile_m,
+                                       int tile_n, int tile_k, int ring) {
+  if (!p || M < 0 || N < 0 || K < 0 || tile_m <= 0 || tile_n <= 0 || tile_k <= 0 || ring < 1 ||
+      p->n_units <= 0 || !(p->load_throughput > 0) || !(p->compute_throughput > 0))
+    return -1.0;
+  const double t_a = (double)tile_m * tile_k / p->load_throughput + p->load_latency;
+  const double t_b = (double)tile_k * tile_n / p->load_throughput + p->load_latency;
+  const double t_m = (double)tile_m * tile_n * tile_k / p->compute_throughput + p->compute_latency;
+  const int64_t S = cdiv(K, tile_k);
+  const int64_t W = cdiv(cdiv(M, tile_m) * cdiv(N, tile_n), p->n_units);
+  if (S > (1 << 30)) return -1.0;
+  const double wave = ws_model_stage_times((int)S, ring, t_a, t_b, t_m, nullptr, nullptr, nullptr,
+                                           nullptr);
+  return (wave + p->t_epilogue) * (double)W + p->t_init;
+}
+
+extern "C" int ws_model_two_point(double size1, double time1, double size2, double time2,
+                                  double* throughput, double* latency) {
+  if (size1 == size2 || time1 == time2) return 1;
+  const double thr = (size1 - size2) / (time1 - time2);
+  if (throughput) *throughput = thr;
+  if (latency) *latency = time1 - size1 / thr;
+  return 0;
+}
+
+extern "C" void ws_model_default(ws_model_params* p, int cus) {
+  if (!p) return;
+  // Two-point calibration on MI355X from the kernel's own stage trace
+  // (ring depth 1, so loads and MATH never overlap); see the GEMM tests'
+  // calibration record for the measurements.
+  p->load_throughput = 16000.0;
+  p->load_latency = 1.0;
+  p->compute_throughput = 4.0e6;
+  p->compute_latency = 0.05;
+  p->t_epilogue = 1.0;
+  p->t_init = 5.0;
+  p->n_units = cus > 0 ? cus : 256;
+}
+
+extern "C" int ws_gemm_choose(const ws_model_params* p, int M, int N, int K, int* tile_m,
+                              int* tile_n, int* tile_k, int* ring) {
+  if (M < 0 || N < 0 || K < 0) return INVALID;
+  ws_model_params def;
+  if (!p) {
+    ws_model_default(&def, device_cus());
+    p = &def;
+  }
+  int best = -1;
+  double best_t = 0.0;
+  for (int i = 0; i < N_VARIANTS; ++i) {
+    const Variant& v = VARIANTS[i];
+    const double t = ws_model_launch_time(p, M, N, K, v.tm, v.tn, v.tk, v.ring);
+    if (t < 0) continue;
+    if (best < 0 || t < best_t) {
+      best = i;
+      best_t = t;
+    }
+  }
+  if (best < 0) return INVALID;
+  if (tile_m) *tile_m = VARIANTS[best].tm;
+  if (tile_n) *tile_n = VARIANTS[best].tn;
+  if (tile_k) *tile_k = VARIANTS[best].tk;
+  if (ring) *ring = VARIANTS[best].ring;
+  return OK;
+}
+
+extern "C" int ws_gemm(const void* a, const void* b, void* c, int M, int N, int K, int tile_m,
+                       int tile_n, int tile_k, int ring, unsigned long long* trace, int* status,
+                       void* stream) {
+  if (M < 0 || N < 0 || K < 0) return INVALID;
+  if (M == 0 || N == 0) return OK;
+  // with K == 0 the inputs are empty and not examined
+  if (!c || (K > 0 && (!a || !b))) return INVALID;
+  if ((N % 8) || (K % 8)) return UNSUPPORTED;
+  if (!aligned16(c) || (K > 0 && (!aligned16(a) || !aligned16(b)))) return UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (((int64_t)M + 256) * K * 2 >= lim || ((int64_t)K + 128) * N * 2 >= lim ||
+      (int64_t)M * N * 2 >= lim)
+    return UNSUPPORTED;
+  if (K > 0 && (overlap(c, (uint64_t)M * N * 2, a, (uint64_t)M * K * 2) ||
+                overlap(c, (uint64_t)M * N * 2, b, (uint64_t)K * N * 2)))
+    return INVALID;
+  if (tile_m == 0 && tile_n == 0 && tile_k == 0 && ring == 0) {
+    const int st = ws_gemm_choose(nullptr, M, N, K, &tile_m, &tile_n, &tile_k, &ring);
+    if (st != OK) return st;
+  }
+  const Variant* v = find_variant(tile_m, tile_n, tile_k, ring);
+  if (!v) return UNSUPPORTED;
+
+  wsgemm::GemmParams prm;
+  prm.a = static_cast<const _Float16*>(a);
+  prm.b = static_cast<const _Float16*>(b);
+  prm.c = static_cast<_Float16*>(c);
+  prm.trace = trace;
+  prm.status = status;
+  prm.M = M;
+  prm.N = N;
+  prm.K = K;
+  prm.n_tm = (int)cdiv(M, v->tm);
+  prm.n_tn = (int)cdiv(N, v->tn);
+  prm.stages = (int)cdiv(K, v->tk);
+  prm.spin_limit = SPIN_LIMIT;
+  const int64_t grid = (int64_t)prm.n_tm * prm.n_tn;
+  if (grid >= lim) return UNSUPPORTED;
+  const hipError_t e = launch_variant(*v, prm, (unsigned)grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? OK : HIP_FAIL;
+}

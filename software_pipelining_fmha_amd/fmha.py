@@ -35,6 +35,15 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("libfmha.so is not built (%s); run __graft_entry__.build() "
                                "or python -m software_pipelining_fmha_amd.build" % _LIB_PATH)
+        # torch sets up the HIP runtime first: if the library's kernels are
+        # registered before torch initialises HIP, their launches fail with
+        # hipErrorOutOfMemory on the MI355X image this targets.
+        try:
+            import torch
+            if torch.cuda.is_available():
+                torch.cuda.init()
+        except ImportError:  # pragma: no cover
+            pass
         l = ctypes.CDLL(_LIB_PATH)
         l.fmha_fwd.restype = ctypes.c_int
         l.fmha_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float,

@@ -27,6 +27,12 @@ standard_normal draw of the same shape, from
 numpy.random.default_rng(20260000 + c + DOUT_SEED_OFFSET), rounded once to
 float16. The pages give no backward workload, so it reuses the forward
 shapes.
+GEMM (the warp-specialised GEMM of the performance-model page): A [M][K]
+and B [K][N] are float32 standard_normal draws, A first, from
+numpy.random.default_rng(20260900 + c) for GEMM workload c (or the seed a
+test passes), each rounded once to float16. The page measures
+M, N, K in {256, 512, 1024} with T_M, T_N, T_K in {64, 128}; Tawa (CGO'26),
+section V-D, measures FP16 GEMM at M = N = 8192 with K from 256 to 16384.
 """
 from __future__ import annotations
 
@@ -208,3 +214,47 @@ def workload_rows(index: int) -> np.ndarray:
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+GEMM_SEED_BASE = 20260900
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+
+
+GEMM_WORKLOADS = (
+    GemmWorkload("gemm_m256n256k256", 256, 256, 256),
+    GemmWorkload("gemm_m1024n1024k1024", 1024, 1024, 1024),
+    GemmWorkload("gemm_m8192n8192k8192", 8192, 8192, 8192),
+    GemmWorkload("gemm_m8192n8192k1024", 8192, 8192, 1024),
+)
+GEMM_HEADLINE = 2
+
+
+def draw_gemm(M: int, N: int, K: int, seed: int):
+    """A fp16 [M, K] and B fp16 [K, N], row-major."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
+    b = rng.standard_normal((K, N), dtype=np.float32).astype(np.float16)
+    return a, b
+
+
+def gemm_workload_inputs(index: int):
+    w = GEMM_WORKLOADS[index]
+    return draw_gemm(w.M, w.N, w.K, GEMM_SEED_BASE + index)
+
+
+def gemm_sample_rows(M: int, tile_m: int, n: int, seed: int) -> np.ndarray:
+    """Sorted distinct rows: the first and last row of every tile_m block
+    (up to n of them), then seeded random rows up to n in total."""
+    edges = sorted({r for t in range(0, M, tile_m) for r in (t, min(t + tile_m, M) - 1)})
+    rows = set(edges[:n])
+    rng = np.random.default_rng(seed ^ SAMPLE_SEED_XOR)
+    while len(rows) < min(n, M):
+        rows.add(int(rng.integers(0, M)))
+    return np.array(sorted(rows), dtype=np.int64)

@@ -116,14 +116,14 @@ def test_row_subset_and_degenerate_sizes():
 # ---- planted slips ---------------------------------------------------------
 
 MUTANTS = {
-    "last k term dropped": ("for (int64_t k = 0; k < K; ++k) {\n                const double p",
-                            "for (int64_t k = 0; k < K - 1; ++k) {\n                const double p"),
-    "B read transposed": ("jb->b[k * N + n]", "jb->b[n * K + k]"),
+    "last k term dropped": ("for (int64_t k = 0; k < K; ++k) {\n            const double am",
+                            "for (int64_t k = 0; k < K - 1; ++k) {\n            const double am"),
+    "B read transposed": ("jb->b + k * N", "jb->b + k"),
     "A row from the request index": ("jb->a[m * K + k]", "jb->a[r * K + k]"),
     "exponent bias 14": ("e - 25", "e - 24"),
     "subnormal scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "sign dropped": ("return sign ? -v : v;", "return v;"),
-    "magnitude without abs": ("sa += fabs(p);", "sa += p;"),
+    "magnitude without abs": ("ca[n] += fabs(p);", "ca[n] += p;"),
 }
 
 PINS = [
