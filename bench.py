@@ -51,6 +51,8 @@ KERNEL_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_kernel.hpp",
                   "software_pipelining_fmha_amd/csrc/fmha_api.hip")
 BWD_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_bwd_kernel.hpp",)
 FP8_SOURCES = ("software_pipelining_fmha_amd/csrc/fmha_fwd_fp8_kernel.hpp",)
+GEMM_SOURCES = ("software_pipelining_fmha_amd/csrc/ws_gemm_kernel.hpp",
+                "software_pipelining_fmha_amd/csrc/ws_gemm_api.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fmha_fwd_b4h32n16384d128.txt")
 
 
@@ -75,6 +77,10 @@ def kernel_digest() -> str:
 
 def fp8_digest() -> str:
     return _source_digest(FP8_SOURCES + KERNEL_SOURCES)
+
+
+def gemm_digest() -> str:
+    return _source_digest(GEMM_SOURCES)
 
 
 def bwd_digest() -> str:
@@ -325,6 +331,193 @@ def bench_fp8(args) -> int:
     return 0
 
 
+def _gemm_time(torch, fn, stream, reps: int):
+    """Median and all HIP-event times (ms) of `reps` launches of fn()."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s_, e in ev:
+        s_.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    ts = [s_.elapsed_time(e) for s_, e in ev]
+    return float(np.median(ts)), ts
+
+
+def bench_gemm(args) -> int:
+    """The warp-specialised GEMM at one workload: C = A B, fp16, timed per
+    launch with HIP events on the launch stream."""
+    import torch
+
+    from software_pipelining_fmha_amd import ws_gemm
+
+    names = [w.name for w in inputs.GEMM_WORKLOADS]
+    name = args.workload if args.workload in names else inputs.GEMM_WORKLOADS[inputs.GEMM_HEADLINE].name
+    idx = names.index(name)
+    w = inputs.GEMM_WORKLOADS[idx]
+    dev = torch.device("cuda:0")
+    a, b = inputs.gemm_workload_inputs(idx)
+    ta, tb = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    cfg = tuple(int(x) for x in args.gemm_config.split(",")) if args.gemm_config else \
+        ws_gemm.choose(w.M, w.N, w.K)
+    stream = torch.cuda.current_stream(dev)
+    flops = 2.0 * w.M * w.N * w.K
+
+    def step():
+        ws_gemm.gemm(ta, tb, out=c, config=cfg, status=status, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    med, ts = _gemm_time(torch, step, stream, args.steps)
+    wall = time.perf_counter() - t0
+    if int(status.item()) != 0:
+        print("a semaphore wait gave up", file=sys.stderr)
+        return 1
+    avg_ms = float(np.mean(ts))
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    # context: the library GEMM on the same operands (hipBLASLt through torch)
+    lib_ms, _ = _gemm_time(torch, lambda: torch.matmul(ta, tb), stream, max(5, args.steps // 2))
+    result = {
+        "metric": "WS GEMM TFLOPS (fp16, %s) and %% of MFMA peak" % w.name,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "tile": list(cfg[:3]),
+                   "ring": cfg[3], "chosen_by": "explicit" if args.gemm_config else "model",
+                   "flops_per_step": flops, "seed": inputs.GEMM_SEED_BASE + idx},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms_avg": round(avg_ms, 4),
+                     "kernel_ms_min": round(min(ts), 4), "kernel_digest": gemm_digest()},
+        "context": {"torch_matmul_tflops": round(flops / (lib_ms * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = cpu_threads()
+        rows = inputs.gemm_sample_rows(w.M, cfg[0], 96 if w.M > 2048 else w.M, seed=idx)
+        t1 = time.perf_counter()
+        ref, cabs = oracle.gemm_rows(a, b, rows, threads=threads, magnitude=True)
+        dt = time.perf_counter() - t1
+        got = c.cpu().numpy()[rows].astype(np.float64)
+        bar = 2.0 ** -11 * np.abs(ref) + (w.K + 2) * 2.0 ** -24 * cabs + 2.0 ** -24
+        worst = float((np.abs(got - ref) / bar).max())
+        result["cpu_baseline"] = {
+            "value": 2.0 * len(rows) * w.N * w.K / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d rows of C (tile edges first) of %s; %.1f s wall" % (len(rows), w.name, dt)}
+        result["parity"] = {"rows": int(len(rows)), "max_err_over_bar": worst, "pass": bool(worst <= 1.0)}
+    print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        return 1
+    return 0
+
+
+def bench_wsmodel(args) -> int:
+    """The analytic model of the warp-specialised GEMM on this GPU: two-point
+    calibration from the kernel's own stage trace, then predicted against
+    measured launch time over the page's problem space (M, N, K in {256,
+    512, 1024}, T_M, T_N, T_K in {64, 128}, every compiled ring depth), and
+    the chooser's pick against the measured best per problem."""
+    import itertools
+
+    import torch
+
+    from software_pipelining_fmha_amd import ws_gemm
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    tick_us = 0.01  # wall_clock64 runs at 100 MHz
+
+    def operands(M, N, K, seed):
+        a, b = inputs.draw_gemm(M, N, K, seed)
+        return (torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev),
+                torch.empty((M, N), dtype=torch.float16, device=dev))
+
+    # ---- calibration: ring depth 1, so a stage's loads and MATH never overlap
+    calib = {}
+    for cfg, (M, N, K) in (((64, 64, 64, 1), (1024, 1024, 1024)),
+                           ((128, 128, 128, 1), (2048, 2048, 1024))):
+        ta, tb, c = operands(M, N, K, 8000 + cfg[0])
+        S = -(-K // cfg[2])
+        tiles = (M // cfg[0]) * (N // cfg[1])
+        trace = torch.zeros(ws_gemm.trace_words(M, N, K, *cfg[:3]), dtype=torch.int64, device=dev)
+        for _ in range(3):
+            ws_gemm.gemm(ta, tb, out=c, config=cfg, trace=trace, stream=stream)
+        med, _ = _gemm_time(torch, lambda: ws_gemm.gemm(ta, tb, out=c, config=cfg, trace=trace,
+                                                        stream=stream), stream, 5)
+        t = trace.cpu().numpy().reshape(tiles, S + 1, 5).astype(np.float64) * tick_us
+        st = t[:, :S, :]
+        span = t[:, S, 1].max() - t[:, S, 0].min()
+        calib[cfg] = {
+            "load": float(np.mean(st[:, :, 1] - st[:, :, 0])),
+            "math": float(np.mean(st[:, :, 4] - st[:, :, 2])),
+            "epi": float(np.mean(t[:, S, 1] - st[:, S - 1, 4])),
+            "init": float(med * 1e3 - span),
+        }
+    c1, c2 = calib[(64, 64, 64, 1)], calib[(128, 128, 128, 1)]
+    # A and B load together per stage: T_LOAD_A + T_LOAD_B = (T_M T_K + T_K T_N) / thr + 2 lat
+    thr, lat2 = ws_gemm.two_point(64 * 64 + 64 * 64, c1["load"], 128 * 128 + 128 * 128, c2["load"])
+    cthr, clat = ws_gemm.two_point(64.0 ** 3, c1["math"], 128.0 ** 3, c2["math"])
+    p = ws_gemm.ModelParams()
+    p.load_throughput, p.load_latency = thr, lat2 / 2
+    p.compute_throughput, p.compute_latency = cthr, clat
+    p.t_epilogue = (c1["epi"] + c2["epi"]) / 2
+    p.t_init = (c1["init"] + c2["init"]) / 2
+    p.n_units = cus
+
+    # ---- validation over the page's space
+    sizes = (256, 512, 1024)
+    cfgs = [c_ for c_ in ws_gemm.configs() if c_[0] in (64, 128)]
+    rows, errs, regrets = [], [], []
+    for M, N, K in itertools.product(sizes, repeat=3):
+        ta, tb, c = operands(M, N, K, 8100 + M + 3 * N + 7 * K)
+        meas = {}
+        for cfg in cfgs:
+            fn = lambda: ws_gemm.gemm(ta, tb, out=c, config=cfg, stream=stream)  # noqa: E731
+            for _ in range(2):
+                fn()
+            med, _ = _gemm_time(torch, fn, stream, 9)
+            meas[cfg] = med * 1e3
+            pred = ws_gemm.launch_time(p, M, N, K, *cfg)
+            errs.append((pred - meas[cfg]) / meas[cfg])
+            rows.append((M, N, K) + cfg + (meas[cfg], pred))
+        pick = ws_gemm.choose(M, N, K, p)
+        regrets.append(meas[pick] / min(meas.values()) - 1.0)
+    errs = np.array(errs)
+    result = {
+        "metric": "WS model mean |prediction error| over the page's GEMM space", "unit": "%",
+        "value": round(100 * float(np.mean(np.abs(errs))), 2), "higher_is_better": False,
+        "n_gpus": 1, "data": "synthetic",
+        "config": {"workload": "M,N,K in {256,512,1024}; T_M,T_N,T_K in {64,128}; rings 1-4",
+                   "launches": len(rows)},
+        "max_abs_error_pct": round(100 * float(np.max(np.abs(errs))), 2),
+        "median_error_pct": round(100 * float(np.median(errs)), 2),
+        "within_10pct": round(float(np.mean(np.abs(errs) <= 0.10)), 3),
+        "chooser_regret_mean_pct": round(100 * float(np.mean(regrets)), 2),
+        "chooser_regret_max_pct": round(100 * float(np.max(regrets)), 2),
+        "calibration": {"load_throughput_elem_per_us": thr, "load_latency_us": lat2 / 2,
+                        "compute_throughput_mac_per_us": cthr, "compute_latency_us": clat,
+                        "t_epilogue_us": p.t_epilogue, "t_init_us": p.t_init, "n_units": cus,
+                        "points": {"%dx%dx%d_r%d" % k: v for k, v in calib.items()}},
+        "kernel_digest": gemm_digest(),
+    }
+    if args.model_table:
+        with open(args.model_table, "w") as f:
+            f.write("M N K T_M T_N T_K ring measured_us predicted_us\n")
+            for r in rows:
+                f.write("%d %d %d %d %d %d %d %.3f %.3f\n" % r)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def copy_calibration(mib: int, steps: int) -> int:
     """A plain copy kernel of known size: `steps` launches that each read and
     write mib MiB."""
@@ -348,14 +541,21 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=inputs.WORKLOADS[inputs.HEADLINE].name,
-                    choices=[w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.FP8_WORKLOADS])
+                    choices=[w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.FP8_WORKLOADS]
+                    + [w.name for w in inputs.GEMM_WORKLOADS])
     ap.add_argument("--dtype", choices=["f16", "fp8"], default="f16",
                     help="f16 (default) or the FP8 (E4M3) forward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward pass (default) or the backward pass")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "gemm", "wsmodel"],
+                    default="fwd",
+                    help="time the attention forward pass (default) or backward pass, the "
+                         "warp-specialised GEMM, or validate the GEMM's analytic model")
+    ap.add_argument("--gemm-config", default="",
+                    help="T_M,T_N,T_K,ring for --pass gemm (default: the model's pick)")
+    ap.add_argument("--model-table", default="",
+                    help="--pass wsmodel: also write every measured/predicted launch here")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many MiB "
                          "per step (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -377,6 +577,10 @@ def main(argv=None) -> int:
     fmha.lib()  # fail loudly before any work if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.which == "gemm":
+        return bench_gemm(args)
+    if args.which == "wsmodel":
+        return bench_wsmodel(args)
     if args.dtype == "fp8":
         if args.which != "fwd":
             print("the FP8 path is forward only", file=sys.stderr)

@@ -42,10 +42,12 @@ extern "C" {
  *           ws_gemm_choose pick with the built-in MI355X model parameters.
  * trace   : NULL, or a device buffer of ws_gemm_trace_words(...) 64-bit
  *           words that receives per-stage timestamps (100 MHz wall clock):
- *           per workgroup, (S + 1) rows of 4 words. Row i < S: DMA wave
+ *           per workgroup, (S + 1) rows of 5 words. Row i < S: DMA wave
  *           starts issuing stage i; stage i landed and signalled; MATH wave
- *           0 starts stage i; MATH wave 0 releases its slot. Row S: the
- *           workgroup's start, its end, its tile id, 0.
+ *           0 starts stage i; MATH wave 0 releases its slot; MATH wave 0's
+ *           MFMAs of stage i have finished (a traced launch waits for them
+ *           each stage). Row S: the workgroup's start, its end, its tile
+ *           id, 0, 0.
  * status  : NULL, or a device int the caller zeroes; set to 1 if a
  *           semaphore wait gave up (the output is then not valid). A wait
  *           gives up after about 2^22 polls, far beyond any legitimate wait.

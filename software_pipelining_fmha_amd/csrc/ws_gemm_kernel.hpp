@@ -60,13 +60,15 @@ struct GemmParams {
   int spin_limit;             // polls before a wait gives up
 };
 
-// Trace layout, when p.trace is not null: per workgroup w (tile order) a
-// block of (stages + 1) x 4 values of wall_clock64() (100 MHz). Row i < S:
+// Trace layout, when p.trace is not null: per workgroup (launch order) a
+// block of (stages + 1) x 5 values of wall_clock64() (100 MHz). Row i < S:
 // [0] DMA wave starts issuing stage i, [1] DMA wave sees stage i landed and
 // signals it, [2] MATH wave 0 starts stage i, [3] MATH wave 0 releases
-// stage i's slot. Row S: [0] workgroup start, [1] MATH wave 0 done with its
-// stores, [2] the tile id, [3] 0.
-constexpr int TRACE_FIELDS = 4;
+// stage i's slot, [4] MATH wave 0's MFMAs of stage i have finished. Row S:
+// [0] workgroup start, [1] MATH wave 0 done with its stores, [2] the tile
+// id, [3] and [4] 0. Only a traced launch waits for [4] (a register read of
+// the stage's last accumulator), so only it is slowed by it.
+constexpr int TRACE_FIELDS = 5;
 // One DMA wave and four MATH waves.
 constexpr int GEMM_THREADS = 5 * 64;
 
@@ -307,36 +309,66 @@ __global__ __launch_bounds__(GEMM_THREADS) void ws_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
+  // Operands of one k-step: A^T fragments by 16-byte reads, B^T fragments
+  // by pairs of transposing reads.
+  auto read_step = [&](const lds_char* slot, int s, half8 (&af)[T::MB], half8 (&bf)[T::NB])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < T::MB; ++mb)
+      af[mb] = *(const __attribute__((address_space(3))) half8*)(
+          slot + a_row[mb] + 16 * ((2 * s + hh) ^ a_swz[mb]));
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) {
+      const lds_char* src = slot + b_base[nb] + 16 * s * TN * 2;
+      const shortx4 lo = read_tr16(src);
+      const shortx4 hi = read_tr16(src + 4 * TN * 2);
+      bf[nb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  // Software pipeline over k-steps, one step ahead, across stage boundaries:
+  // at the last step of stage i the wave completes stage i's reads, releases
+  // its slot, waits for stage i+1 and reads its first operands, all before
+  // stage i's last MFMAs.
+  static_assert(T::KSTEPS % 2 == 0, "k-step buffers alternate within a stage");
+  half8 af[2][T::MB], bf[2][T::NB];
   bool ok = true;
+  if (S > 0) {
+    ok = wait_geq(full, 1u, limit);
+    if (trace && wave == 0 && lane == 0) trace[2] = wall_clock64();
+    read_step(ring, 0, af[0], bf[0]);
+  }
   for (int i = 0; i < S; ++i) {
-    ok = ok && wait_geq(full, (uint32_t)(i + 1), limit);
-    if (trace && wave == 0 && lane == 0) trace[i * TRACE_FIELDS + 2] = wall_clock64();
     const lds_char* const slot = ring + (i % RING) * T::SLOT_BYTES;
 #pragma unroll
     for (int s = 0; s < T::KSTEPS; ++s) {
-      half8 af[T::MB], bf[T::NB];
-#pragma unroll
-      for (int mb = 0; mb < T::MB; ++mb)
-        af[mb] = *(const __attribute__((address_space(3))) half8*)(
-            slot + a_row[mb] + 16 * ((2 * s + hh) ^ a_swz[mb]));
-#pragma unroll
-      for (int nb = 0; nb < T::NB; ++nb) {
-        const lds_char* src = slot + b_base[nb] + 16 * s * TN * 2;
-        const shortx4 lo = read_tr16(src);
-        const shortx4 hi = read_tr16(src + 4 * TN * 2);
-        bf[nb] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-      if (s == T::KSTEPS - 1) {
-        // every operand of this slot is in registers: release it
+      const int cur = s & 1;
+      if (s + 1 < T::KSTEPS) {
+        read_step(slot, s + 1, af[cur ^ 1], bf[cur ^ 1]);
+      } else {
+        // every operand of stage i is in registers: release its slot first
+        // (with one slot, stage i+1 can only land after that)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (lane == 0) store_counter(released + 4 * wave, (uint32_t)(i + 1));
         if (trace && wave == 0 && lane == 0) trace[i * TRACE_FIELDS + 3] = wall_clock64();
+        if (i + 1 < S) {
+          ok = ok && wait_geq(full, (uint32_t)(i + 2), limit);
+          if (trace && wave == 0 && lane == 0) trace[(i + 1) * TRACE_FIELDS + 2] = wall_clock64();
+          read_step(ring + ((i + 1) % RING) * T::SLOT_BYTES, 0, af[0], bf[0]);
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < T::MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
-          acc[mb][nb] = mfma16(bf[nb], af[mb], acc[mb][nb]);
+          acc[mb][nb] = mfma16(bf[cur][nb], af[cur][mb], acc[mb][nb]);
+    }
+    if (trace && wave == 0) {
+      // MFMAs retire in order: reading the last one's result waits for all
+      float last;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(last) : "v"(acc[T::MB - 1][T::NB - 1][15]));
+      asm volatile("" ::"v"(last));
+      if (lane == 0) trace[i * TRACE_FIELDS + 4] = wall_clock64();
     }
   }
 
@@ -364,6 +396,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void ws_gemm_kernel(GemmParams p) {
     trace[S * TRACE_FIELDS + 1] = wall_clock64();
     trace[S * TRACE_FIELDS + 2] = (unsigned long long)t;
     trace[S * TRACE_FIELDS + 3] = 0;
+    trace[S * TRACE_FIELDS + 4] = 0;
   }
   if (!ok && p.status && lane == 0) *p.status = 1;
 }

@@ -123,9 +123,9 @@ def test_ring_depth_does_not_change_bits(device):
                                  (128, 128, 128, 2)], ids=lambda c: "t%dx%dx%d_r%d" % c)
 def test_trace_obeys_the_semaphores(cfg, device):
     """Per workgroup and stage i: the DMA wave issues a stage before it
-    lands, MATH wave 0 starts it after it landed and releases it after it
-    started, and stage i is issued only after stage i - ring was released
-    (by MATH wave 0 at least)."""
+    lands, MATH wave 0 starts it after it landed, releases it after it
+    started and finishes its MFMAs after that; stage i is issued only after
+    stage i - ring was released (by MATH wave 0 at least)."""
     M, N, K = 512, 512, 1024
     tm, tn, tk, ring = cfg
     S = -(-K // tk)
@@ -134,12 +134,14 @@ def test_trace_obeys_the_semaphores(cfg, device):
     c, tr = run(a, b, cfg, trace_words=words)
     check(c, a, b, np.arange(0, M, 7), "traced %s" % (cfg,))
     tiles = (M // tm) * (N // tn)
-    t = tr.reshape(tiles, S + 1, 4)
+    t = tr.reshape(tiles, S + 1, 5)
     st = t[:, :S, :]
     assert (st > 0).all()
     assert (st[:, :, 1] >= st[:, :, 0]).all()   # landed after issued
     assert (st[:, :, 2] >= st[:, :, 1]).all()   # MATH starts after landed
     assert (st[:, :, 3] >= st[:, :, 2]).all()   # released after started
+    assert (st[:, :, 4] >= st[:, :, 3]).all()   # MFMAs end after the release
+    assert (st[:, 1:, 2] >= st[:, :-1, 3]).all()  # next stage starts after this release
     if S > ring:
         assert (st[:, ring:, 0] >= st[:, :-ring, 3]).all()  # slot reuse waits for release
     assert (t[:, S, 1] >= st[:, S - 1, 3]).all()

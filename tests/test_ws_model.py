@@ -106,7 +106,7 @@ def test_config_list():
 
 
 def test_trace_words():
-    assert ws_gemm.trace_words(256, 256, 1024, 128, 128, 64) == 4 * (16 + 1) * 4
+    assert ws_gemm.trace_words(256, 256, 1024, 128, 128, 64) == 4 * (16 + 1) * 5
     assert ws_gemm.trace_words(0, 256, 1024, 128, 128, 64) == 0
 
 
