@@ -55,6 +55,9 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 constexpr float RESCALE_LOG2 = 8.0f;
 // MFMA slots by which an LDS operand read precedes its MFMA.
 constexpr int OPERAND_AHEAD = 4;
+// U MFMAs at the head of a matrix-core interval whose operands are read in
+// the wave's preceding vector interval.
+constexpr int LEAD_U = 2;
 
 struct Params {
   const _Float16* q;
@@ -425,39 +428,64 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // T MFMAs, so consecutive MFMAs never share an accumulator. Each
   // LDS operand is read OPERAND_AHEAD slots before its MFMA; scheduling
   // barriers keep that order, so each MFMA waits only for its own operand.
+  // Slot order: the first LEAD_U slots are U MFMAs, whose V^T operands the
+  // wave already read at the end of its vector interval (V^T_{j-1} is
+  // complete one interval before U_{j-1}; K_j is complete only when this
+  // interval starts). Then T and U alternate, and the last LEAD_U slots are
+  // T MFMAs. T slot n is key block n % KB at k-step n / KB and U slot n is
+  // d block n % DBLK at k-step n / DBLK, so consecutive MFMAs of one kind
+  // never share an accumulator either.
+  constexpr int NPV = T::PSTEPS * T::DBLK;
+  constexpr int NM = 2 * NPV;
+  static_assert(NPV == T::KSTEPS * T::KB, "as many U as T MFMAs");
+  constexpr int AHEAD = OPERAND_AHEAD;
+  static_assert(LEAD_U <= AHEAD && LEAD_U < NPV, "lead operands fit the read-ahead ring");
+  // slot i -> (is U, index among its kind)
+  auto slot_is_u = [](int i) constexpr {
+    return i < LEAD_U ? true : (i >= NM - LEAD_U ? false : ((i - LEAD_U) & 1) == 1);
+  };
+  auto slot_n = [](int i) constexpr {
+    return i < LEAD_U ? i : (i >= NM - LEAD_U ? i - NPV : (i - LEAD_U) / 2 + (((i - LEAD_U) & 1) ? LEAD_U : 0));
+  };
+  auto u_operand = [&](const lds_char* vs, int n) __attribute__((always_inline)) {
+    const int st = n / T::DBLK, b = n % T::DBLK;
+    return *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * st);
+  };
+  auto t_operand = [&](const lds_char* ks, int n) __attribute__((always_inline)) {
+    const int kb = n % T::KB, st = n / T::KB;
+    return *(const lds_half8*)(ks + k_rd[st] + kb * K_BLOCK_BYTES);
+  };
+  half8 ring[AHEAD];
+  // End of a vector interval: the lead U operands of the next matrix-core
+  // interval, U_{j-1} with V^T slot PREV of that interval.
+  auto prefetch_lead = [&](auto u_tag) __attribute__((always_inline)) {
+    constexpr int PREV = (decltype(u_tag)::value + 2) % 3;
+    const lds_char* vs = v_ring + PREV * T::VT_BYTES + vt_rd;
+#pragma unroll
+    for (int i = 0; i < LEAD_U; ++i) ring[i] = u_operand(vs, i);
+  };
   auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
     constexpr int U = decltype(u_tag)::value;
     constexpr int PREV = (U + 2) % 3;
-    constexpr int NPV = T::PSTEPS * T::DBLK;
-    constexpr int NM = 2 * NPV;
-    static_assert(NPV == T::KSTEPS * T::KB, "U and T MFMAs alternate");
-    constexpr int AHEAD = OPERAND_AHEAD;
     const lds_char* ks = k_ring + U * T::TILE_BYTES;
     const lds_char* vs = v_ring + PREV * T::VT_BYTES + vt_rd;
     auto operand = [&](int i) __attribute__((always_inline)) {
-      const int n = i >> 1;
-      if ((i & 1) == 0) {
-        const int st = n / T::DBLK, b = n % T::DBLK;
-        return *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * st);
-      }
-      const int kb = n / T::KSTEPS, st = n % T::KSTEPS;
-      return *(const lds_half8*)(ks + k_rd[st] + kb * K_BLOCK_BYTES);
+      return slot_is_u(i) ? u_operand(vs, slot_n(i)) : t_operand(ks, slot_n(i));
     };
-    half8 ring[AHEAD];
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) ring[i] = operand(i);
+    for (int i = LEAD_U; i < AHEAD; ++i) ring[i] = operand(i);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const half8 a = ring[i % AHEAD];
       if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
-      const int n = i >> 1;
-      if ((i & 1) == 0) {
+      const int n = slot_n(i);
+      if (slot_is_u(i)) {
         const int st = n / T::DBLK, b = n % T::DBLK;
         oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st], oacc[b], 0, 0, 0);
         if (b == T::DBLK - 1) row_sum(st);
       } else {
-        const int kb = n / T::KSTEPS, st = n % T::KSTEPS;
+        const int kb = n % T::KB, st = n / T::KB;
         const floatx16 c = st == 0 ? floatx16{} : sacc[kb];
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[st], c, 0, 0, 0);
       }
@@ -519,6 +547,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     if constexpr (decltype(exact_tag)::value) softmax(j);
     else softmax_fast(j);
     tr_write(j + 1);
+    prefetch_lead(std::integral_constant<int, (decltype(u_tag)::value + 1) % 3>{});
     vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
@@ -545,6 +574,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     mfma_sync();
     produce(0);
     if (n_wave > 0) softmax(0);
+    prefetch_lead(U1{});
     vector_sync();
     // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
     int j = 1;
