@@ -162,15 +162,18 @@ extern "C" int ws_model_two_point(double size1, double time1, double size2, doub
 
 extern "C" void ws_model_default(ws_model_params* p, int cus) {
   if (!p) return;
-  // Two-point calibration on MI355X from the kernel's own stage trace
-  // (ring depth 1, so loads and MATH never overlap); see the GEMM tests'
-  // calibration record for the measurements.
-  p->load_throughput = 16000.0;
-  p->load_latency = 1.0;
-  p->compute_throughput = 4.0e6;
-  p->compute_latency = 0.05;
-  p->t_epilogue = 1.0;
-  p->t_init = 5.0;
+  // Two-point calibration on MI355X from the kernel's own stage trace, at
+  // ring depth 1 so that loads and MATH never overlap: tiles 64x64x64 on
+  // 1024^3 and 128x128x128 on 2048x2048x1024, each filling every CU once.
+  // Load per stage 0.319 and 1.166 us, MATH 0.354 and 0.974 us, epilogue
+  // 0.238 and 1.726 us (the constant is their mean), launch minus the traced
+  // span 4.21 and 4.72 us (mean).
+  p->load_throughput = 29027.0;  // elements per us, A and B together
+  p->load_latency = 0.0183;
+  p->compute_throughput = 2.957e6;  // multiply-adds per us
+  p->compute_latency = 0.265;
+  p->t_epilogue = 0.982;
+  p->t_init = 4.462;
   p->n_units = cus > 0 ? cus : 256;
 }
 
