@@ -127,7 +127,7 @@ int launch_bwd(const fmha::BwdParams& prm, hipStream_t stream) {
                       dim3(prm.total_wg), dim3(fmha::DkdvTile<D>::THREADS), args, 0, stream);
   if (e != hipSuccess) return FMHA_ERR_HIP;
   e = hipLaunchKernel(reinterpret_cast<const void*>(&fmha::fmha_bwd_dq_kernel<D, CAUSAL>),
-                      dim3(prm.total_wg), dim3(T::THREADS), args, 0, stream);
+                      dim3(prm.total_wg), dim3(fmha::DqTile<D>::THREADS), args, 0, stream);
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
 

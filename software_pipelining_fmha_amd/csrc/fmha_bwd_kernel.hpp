@@ -23,12 +23,12 @@
 // no workspace beyond D and lse is needed and results are deterministic; the
 // price is S and dP computed twice (7 matrix products instead of 5).
 //
-// Streamed tiles go HBM -> registers -> LDS (the load of step t+1 is in
-// flight during the compute of step t) into a two-slot ring, as [row][d]
-// with 16-byte chunk c of row r at chunk c ^ swz(r). One layout serves both
-// reads: MFMA A operands of whole rows (ds_read_b128) and transposed A
-// operands (ds_read_b64_tr_b16, 8 rows of one d column), both free of LDS
-// bank conflicts.
+// Streamed tiles land in a two-slot LDS ring (the load of step t+1 is in
+// flight during the compute of step t) as [row][d] with 16-byte chunk c of
+// row r at chunk c ^ swz(r): through registers in the dK/dV kernel, by
+// LDS-DMA in the dQ kernel. One layout serves both reads: MFMA A operands of
+// whole rows (ds_read_b128) and transposed A operands (ds_read_b64_tr_b16,
+// 8 rows of one d column), both free of LDS bank conflicts.
 #pragma once
 
 #include "fmha_fwd_kernel.hpp"
@@ -502,12 +502,69 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dQ: a workgroup owns 128 queries and streams the key tiles.
 // ---------------------------------------------------------------------------
+// Four waves of 32 queries; two workgroups share a CU. Key and value tiles
+// of 64 rows stream by LDS-DMA (16 bytes per lane straight into LDS, no
+// register staging) into a two-slot ring; each wave issues a quarter of each
+// tile. The step loop is unrolled by two so that both slots are compile-time
+// offsets, which keeps the compiler from waiting for the DMA in flight
+// before reading the other slot.
+template <int D>
+struct DqTile {
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int RW = 32;               // queries a wave owns
+  static constexpr int BT = WAVES * RW;       // queries a workgroup owns
+  static constexpr int BS = 64;               // keys per step
+  static constexpr int KB = BS / 32;          // 32-key blocks per step
+  static constexpr int KSTEPS = D / 16;       // MFMA k-steps over d
+  static constexpr int DBLK = D / 32;         // 32-row blocks of dQ^T
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BS * D * 2;
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;  // K tile, then V tile
+  static constexpr int LDS_BYTES = 2 * SLOT_BYTES;
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // wave-wide 16-byte-per-lane loads
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;
+  static_assert(LOADS_PER_WAVE * WAVES == LOADS_PER_TILE, "tile loads split over the waves");
+  static_assert(BT == BwdTile<D>::BT, "the dQ grid tiles 128 queries like the other kernels");
+};
+
+// The four transposed A operands (16-key k-steps 0..3) of one 32-row d
+// block of K^T: eight ds_read_b64_tr_b16 in one asm block that also waits
+// for them. As a builtin the compiler cannot tell that these reads miss the
+// slot an LDS-DMA is filling, and waits for every DMA in flight before each.
+// a0 and a1 address the two 4-row halves of k-step 0; k-step ks adds
+// 16 rows (KS_BYTES).
+template <int KS_BYTES>
+__device__ __forceinline__ void tr_block4(uint32_t a0, uint32_t a1, half8 (&out)[4]) {
+  shortx4 r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(a0), "v"(a1), "n"(KS_BYTES), "n"(2 * KS_BYTES), "n"(3 * KS_BYTES)
+      : "memory");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const half4 lo = __builtin_bit_cast(half4, r[2 * k]), hi = __builtin_bit_cast(half4, r[2 * k + 1]);
+    out[k] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(BwdTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdParams p) {
-  using T = BwdTile<D>;
-  using S = Stream<D>;
+__global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdParams p) {
+  using T = DqTile<D>;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) half8 lds_half8;
   __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
-  typename S::lds_char* const smem = (typename S::lds_char*)smem_raw;
+  lds_char* const smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -548,61 +605,91 @@ __global__ __launch_bounds__(BwdTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(Bwd
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqt[b][i] = 0.f;
 
-  S st;
-  st.init(tid);
+  // DMA sources: load L of a tile fills LDS chunks 64 L .. 64 L + 63, one per
+  // lane; chunk x = row * CPR + pos holds global chunk pos ^ swz(row) of that
+  // row (the swizzle is an involution on chunk indices).
+  int src[T::LOADS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+    const int x = 64 * (wave * T::LOADS_PER_WAVE + i) + lane;
+    const int row = x / T::CPR, pos = x % T::CPR;
+    src[i] = (row * D + 8 * (pos ^ bwd_swz<D>(row))) * 2;
+  }
+  auto fetch = [&](int step, auto slot_tag) __attribute__((always_inline)) {
+    lds_char* dst = smem + decltype(slot_tag)::value * T::SLOT_BYTES + wave * T::LOADS_PER_WAVE * 1024;
+    const int base = step * T::BS * D * 2;
+#pragma unroll
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+      load16_to_lds(rk, base + src[i], dst + i * 1024);
+      load16_to_lds(rv, base + src[i], dst + T::TILE_BYTES + i * 1024);
+    }
+  };
+
   Offsets<D> off;
   off.init(lane);
   const float c2 = p.scale_log2;
 
   const int k_end = CAUSAL ? min(N, q0 + T::BT) : N;
   const int n_steps = (k_end + T::BS - 1) / T::BS;
-  // the ring carries K and V tiles; its statistics slots stay unused
-  st.template load<false>(rk, rv, rD, rL, 0, tid);
-  st.template store<false>(smem, tid);
 
-  for (int step = 0; step < n_steps; ++step) {
-    __syncthreads();
+  // One step: wait until this wave's part of tile `step` has landed, then a
+  // barrier (every part has landed, and every wave is done with the other
+  // slot); start the next tile's DMA into the other slot; compute.
+  auto run_step = [&](int step, auto cur_tag, auto nxt_tag) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (step + 1 < n_steps) fetch(step + 1, nxt_tag);
     const int k_s = step * T::BS;
-    if (step + 1 < n_steps) st.template load<false>(rk, rv, rD, rL, k_s + T::BS, tid);
-    const typename S::lds_char* sk = smem + (step & 1) * T::SLOT_BYTES;
-    const typename S::lds_char* sv = sk + T::TILE_BYTES;
-
-    if (!CAUSAL || k_s <= qw0 + T::RW - 1) {
-      // S^T = K Q^T and dP^T = V dO^T: lane = query, register i = key
-      // k_s + 16 (i / 8) + 8 hh + i % 8.
-      floatx16 s, dp;
+    const lds_char* sk = smem + decltype(cur_tag)::value * T::SLOT_BYTES;
+    const lds_char* sv = sk + T::TILE_BYTES;
+    if (CAUSAL && k_s > qw0 + T::RW - 1) return;  // every key of the step is after every query
+    // S^T = K Q^T and dP^T = V dO^T per 32-key block: lane = query, register
+    // i = key k_s + 32 kb + 16 (i / 8) + 8 hh + i % 8.
+    floatx16 s[T::KB], dp[T::KB];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+    for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int k = 0; k < T::KSTEPS; ++k)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sk + off.nat[k]),
-                                                   qf[k], s, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
 #pragma unroll
-      for (int k = 0; k < T::KSTEPS; ++k)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const typename S::lds_half8*)(sv + off.nat[k]),
-                                                    dof[k], dp, 0, 0, 0);
-      const bool edge = (CAUSAL && k_s + T::BS - 1 > qw0) || k_s + T::BS > N;
-      half8 dsf[2];
+    for (int k = 0; k < T::KSTEPS; ++k)
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const int o = off.nat[k] + kb * 32 * D * 2;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sk + o), qf[k], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sv + o), dof[k], dp[kb], 0, 0, 0);
+      }
+    const bool edge = (CAUSAL && k_s + T::BS - 1 > qw0) || k_s + T::BS > N;
+    half8 dsf[2 * T::KB];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, nl2));
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, nl2));
         if (edge) {
-          const int kk = k_s + 16 * (i >> 3) + 8 * hh + (i & 7);
+          const int kk = k_s + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
           if ((CAUSAL && kk > qrow) || kk >= N) pv = 0.f;
         }
-        dsf[i >> 3][i & 7] = (_Float16)(pv * (dp[i] - Dq));
+        dsf[2 * kb + (i >> 3)][i & 7] = (_Float16)(pv * (dp[kb][i] - Dq));
       }
-      // dQ^T += K^T dS^T (k = keys, two k-steps)
+    // dQ^T += K^T dS^T (k = keys, 16 per k-step)
+    static_assert(2 * T::KB == 4, "one transposed-read block covers the step's keys");
+    const uint32_t skb = (uint32_t)(uintptr_t)sk;
 #pragma unroll
-      for (int b = 0; b < T::DBLK; ++b)
+    for (int b = 0; b < T::DBLK; ++b) {
+      half8 a[4];
+      tr_block4<16 * D * 2>(skb + off.tr[b][0], skb + off.tr[b][1], a);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const half8 a = tr_pair(sk, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
-          dqt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsf[ks], dqt[b], 0, 0, 0);
-        }
+      for (int ks = 0; ks < 4; ++ks)
+        dqt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], dsf[ks], dqt[b], 0, 0, 0);
     }
-    if (step + 1 < n_steps) st.template store<false>(smem + ((step + 1) & 1) * T::SLOT_BYTES, tid);
+  };
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  if (n_steps > 0) fetch(0, Slot0{});
+  for (int step = 0; step < n_steps; step += 2) {
+    run_step(step, Slot0{}, Slot1{});
+    if (step + 1 < n_steps) run_step(step + 1, Slot1{}, Slot0{});
   }
+  // no DMA is in flight past the last step (it issues none)
 
   if (qrow < N) {
     _Float16* dqr = p.dq + head + (size_t)qrow * D;
