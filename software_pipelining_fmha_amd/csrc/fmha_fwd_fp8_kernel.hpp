@@ -5,9 +5,13 @@
 // products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, fp32
 // accumulate, unit block scales), at twice the FP16 MFMA rate:
 // - T stage, S^T = K Q^T: 2 key blocks x 2 k-steps of 64 bytes of d;
-// - C stage: the FP16 kernel's online softmax with lazy rescale, on fp32
-//   scores; the weights are rounded to E4M3 (p <= 2^RESCALE_LOG2 = 256 stays
-//   below E4M3's largest finite value, 448);
+// - C stage: an exact pass (running max with lazy rescale, p <=
+//   2^RESCALE_LOG2 = 256) and, as in the FP16 kernel, a fast pass whose
+//   exponent reference stays at key tile 0's row max (no row max
+//   afterwards). The weights are rounded to E4M3, whose conversion turns
+//   values from 480 up into NaN (there is no infinity), so a fast-pass
+//   overflow shows as a NaN row sum and the tile reruns exactly. Each
+//   workgroup picks the pass from what its first tile shows (Fp8Pass);
 // - U stage, O^T += V^T P^T: one MFMA per 32-row block of d per 64-key tile.
 // Row sums of the E4M3 weights run on v_mfma_scale_f32_16x16x128_f8f6f4 with
 // a 0/1 A operand, so O is normalised by exactly the weights that multiply V.
@@ -79,8 +83,18 @@ __device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The workgroup's choice of pass, kept across its tiles. E4M3's range is
+// small (weights overflow past about 2^8.9 of the reference), so inputs with
+// sharp softmax rows overflow the fast pass on most tiles, and a fast pass
+// plus a rerun costs more than the exact pass alone. So a fast tile that
+// overflows reruns exactly and switches the workgroup to the exact pass for
+// the rest of the launch. The causal kernel holds the exact pass only: with
+// both passes compiled in, its exact pass ran 5% slower on sharp inputs.
+enum Fp8Pass { FP8_FAST = 1, FP8_EXACT = 2 };
+
 template <bool CAUSAL>
-__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw) {
+__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw,
+                                             int& pass) {
   using T = Fp8Tile;
   constexpr int D = T::D;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -257,6 +271,11 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       exp_pack();
     }
   };
+  // Fast C stage: weights against the fixed reference, no row max.
+  auto softmax_fast = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    exp_pack();
+  };
   // T stage alone (tile 0): S^T = K_0 Q^T.
   auto qk = [&]() __attribute__((always_inline)) {
     const lds_char* ks = k_ring;
@@ -364,13 +383,14 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     fetch_k(j + 3);
     fetch_v(j + 2);
   };
-  auto steady = [&](int j, auto u_tag) __attribute__((always_inline)) {
+  auto steady = [&](int j, auto u_tag, auto exact_tag) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     mfma_interval(u_tag);
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     produce_issue(j);
-    softmax(j);
+    if constexpr (decltype(exact_tag)::value) softmax(j);
+    else softmax_fast(j);
     vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
@@ -378,49 +398,82 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
   using U2 = std::integral_constant<int, 2>;
   using U3 = std::integral_constant<int, 3>;
 
-  fetch_k(0);
-  fetch_k(1);
-  fetch_k(2);
-  fetch_v(0);
-  fetch_v(1);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  if (group == 1) sync();
+  // The whole K/V pipeline; the fast variant forms no row max after tile 0.
+  auto run_pipeline = [&](auto exact_tag) __attribute__((always_inline)) {
+    fetch_k(0);
+    fetch_k(1);
+    fetch_k(2);
+    fetch_v(0);
+    fetch_v(1);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (group == 1) sync();
 
-  // j = 0: T_0, then C_0
-  if (n_wave > 0) qk();
-  mfma_sync();
-  produce_issue(0);
-  if (n_wave > 0) softmax(0);
-  vector_sync();
-  int j = 1;
-  for (; j + 4 <= n_wave; j += 4) {
-    steady(j, U1{});
-    steady(j + 1, U2{});
-    steady(j + 2, U3{});
-    steady(j + 3, U0{});
-  }
-  if (j < n_wave) {
-    steady(j, U1{});
-    ++j;
+    // j = 0: T_0, then C_0 (exact: it sets the reference)
+    if (n_wave > 0) qk();
+    mfma_sync();
+    produce_issue(0);
+    if (n_wave > 0) softmax(0);
+    vector_sync();
+    int j = 1;
+    for (; j + 4 <= n_wave; j += 4) {
+      steady(j, U1{}, exact_tag);
+      steady(j + 1, U2{}, exact_tag);
+      steady(j + 2, U3{}, exact_tag);
+      steady(j + 3, U0{}, exact_tag);
+    }
     if (j < n_wave) {
-      steady(j, U2{});
+      steady(j, U1{}, exact_tag);
       ++j;
       if (j < n_wave) {
-        steady(j, U3{});
+        steady(j, U2{}, exact_tag);
         ++j;
+        if (j < n_wave) {
+          steady(j, U3{}, exact_tag);
+          ++j;
+        }
       }
     }
+    // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
+    // which the wave still loads its share of the workgroup's tiles
+    for (; j <= n_kv; ++j) {
+      if (j == n_wave && j >= 1) pv(j - 1);
+      mfma_sync();
+      produce_issue(j);
+      vector_sync();
+    }
+    if (group == 0) sync();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // true in every wave if `mine` holds in some lane of some wave. The flags
+  // sit in the K ring, which trailing DMAs of other waves may still be
+  // writing until every wave has passed its vmcnt(0).
+  auto any_wave = [&](bool mine) __attribute__((always_inline)) {
+    const bool bad = __builtin_amdgcn_ballot_w64(mine) != 0;
+    sync();
+    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)k_ring;
+    if (lane == 0) flags[wave] = bad ? 1 : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < T::WAVES; ++w) any |= flags[w];
+    any = __builtin_amdgcn_readfirstlane(any);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    return any != 0;
+  };
+  if (!CAUSAL && pass == FP8_FAST) {
+    run_pipeline(std::integral_constant<bool, CAUSAL>{});
+    // A weight that overflowed E4M3 is NaN, and so is its row sum.
+    if (any_wave(!(sum_halves(lacc[0]) < INFINITY))) {
+#pragma unroll
+      for (int b = 0; b < T::DBLK; ++b) oacc[b] = floatx16{};
+      lacc = floatx4{};
+      m_run = -INFINITY;
+      run_pipeline(std::true_type{});
+      pass = FP8_EXACT;
+    }
+  } else {
+    run_pipeline(std::true_type{});
   }
-  // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
-  // which the wave still loads its share of the workgroup's tiles
-  for (; j <= n_kv; ++j) {
-    if (j == n_wave && j >= 1) pv(j - 1);
-    mfma_sync();
-    produce_issue(j);
-    vector_sync();
-  }
-  if (group == 0) sync();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = descale_v O_acc / l, lse = (m + log2 l) ln 2 ---------------
   // register i of block b holds d = 32 b + 8 (i / 4) + 4 hh + i % 4
@@ -449,10 +502,11 @@ __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Pa
   const int G = p.total_wg;
   const int per = G >> 3, rem = G & 7;
   const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
+  int pass = CAUSAL ? FP8_EXACT : FP8_FAST;
   for (int r = 0; r * (int)gridDim.x < G; ++r) {
     const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
     if (tile >= G) break;
-    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw);
+    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw, pass);
   }
 }
 

@@ -139,6 +139,98 @@ def test_fp8_uniform_keys_every_row(device):
     assert (err <= E_MFMA * a + 1e-5).all()
 
 
+def _quantized(q, k, v):
+    """Per-tensor E4M3 quantization of float32 q, k, v."""
+    b, sc = zip(*(inputs.quantize_e4m3(x) for x in (q, k, v)))
+    return tuple(b), tuple(sc)
+
+
+def _base2_gap(b, sc, rows, scale):
+    """For each of `rows` (query rows of head (0, 0)): the best score past the
+    first 64 keys minus the best of the first 64, in base-2 units."""
+    q, k = (oracle.e4m3_to_double(x[0, 0]) * float(s) for x, s in zip(b[:2], sc[:2]))
+    s = float(scale) * q[rows] @ k.T
+    return (s[:, 64:].max(axis=1) - s[:, :64].max(axis=1)) / math.log(2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_late_scores_overflow_rerun(causal, device):
+    """For one block of query rows, a key past the first 64 scores about 2^18
+    above every key of the first 64. Formed against the first tile's row
+    max, its weight overflows E4M3 (NaN), so the workgroup reruns with the
+    running max. Every row is compared with the oracle."""
+    B, H, N, d = 1, 2, 700, 128
+    rng = np.random.default_rng(6500 + causal)
+    q, k, v = (rng.standard_normal((B, H, N, d), dtype=np.float32) for _ in range(3))
+    q[:, 0, 300:340, 7] = 12
+    k[:, 0, 64:, 7] = 12
+    b, sc = _quantized(q, k, v)
+    scale = np.float32(1 / math.sqrt(d))
+    gap = _base2_gap(b, sc, np.arange(300, 340), scale)
+    assert gap.min() > 10, "inputs do not reach the overflow case"
+    o, lse = run(b, sc, causal, scale)
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 late-large")
+
+
+def test_fp8_late_scores_inside_e4m3(device):
+    """Keys past the first tile score 2^7.8 to 2^8.7 above the first tile's
+    max: the fast pass's weights stay finite in E4M3 (below 448) and many
+    pass 256, the exact pass's rescale threshold, with no rerun. The late
+    scores are spread over that range so that their weights round
+    independently, as the bar assumes; hundreds of equal weights would all
+    round the same way (by up to 2^-4) in either pass."""
+    B, H, N, d = 1, 1, 640, 128
+    rng = np.random.default_rng(6600)
+    q, k, v = (rng.standard_normal((B, H, N, d), dtype=np.float32) for _ in range(3))
+    q *= np.float32(0.05)
+    k *= np.float32(0.05)
+    scale = np.float32(1 / math.sqrt(d))
+    gap2 = rng.uniform(7.9, 8.6, size=N - 64)  # base-2 gaps of the late keys
+    q[..., 3] = 8
+    k[0, 0, 64:, 3] = (gap2 * math.log(2) / (8 * float(scale))).astype(np.float32)
+    b, sc = _quantized(q, k, v)
+    gap = _base2_gap(b, sc, np.arange(N), scale)
+    assert 7.5 < gap.min() and gap.max() < 8.75, (gap.min(), gap.max())
+    o, lse = run(b, sc, False, scale)
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=False, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 late-inside")
+
+
+def test_fp8_exact_fallback_carries_over_tiles(device):
+    """More query tiles than compute units, with weight overflows in every
+    head of batch 0 (rows 500..539 see a late key about 2^16 above the first
+    key tile). Workgroups whose first tile holds such rows choose the exact
+    pass for all their tiles; others choose the fast pass and, on meeting
+    such a tile later, rerun it exactly and keep the exact pass. The
+    overflow rows and both edges of every tile match the oracle."""
+    import torch
+    B, H, N, d = 3, 31, 1000, 128
+    bm = 256
+    tiles = B * H * (-(-N // bm))
+    assert tiles > torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(6700)
+    q, k, v = (rng.standard_normal((B, H, N, d), dtype=np.float32) for _ in range(3))
+    q[0, :, 500:540, 7] = 12
+    k[0, :, 64:, 7] = 12
+    b, sc = _quantized(q, k, v)
+    scale = np.float32(1 / math.sqrt(d))
+    assert _base2_gap(b, sc, np.arange(500, 540), scale).min() > 10
+    o, lse = run(b, sc, False, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rows = []
+    for bb in range(B):
+        for h in range(H):
+            for t0 in range(0, N, bm):
+                rows += [(bb, h, t0), (bb, h, min(t0 + bm, N) - 1)]
+    rows += [(0, h, i) for h in (0, 17, 30) for i in (500, 519, 539)]
+    rows = np.array(rows, dtype=np.int64)
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=False, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 sticky exact")
+
+
 def test_fp8_deterministic_bitwise(device):
     b, sc = inputs.draw_qkv_fp8(2, 4, 700, 128, seed=6262)
     a1 = run(b, sc, False, np.float32(0.088388))
