@@ -87,20 +87,41 @@ def bwd_digest() -> str:
     return _source_digest(BWD_SOURCES + KERNEL_SOURCES[1:])
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source and this workload; else None."""
+def _recorded_counters(workload: str) -> dict:
+    """key=value pairs of the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source and this workload; else {}."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return {}
     kv = {}
     for line in open(TRAFFIC_FILE):
-        if "=" in line and not line.startswith("#"):
-            key, val = line.split("=", 1)
-            kv[key.strip()] = val.strip()
+        if line.startswith("#"):
+            continue
+        for item in line.split():
+            if "=" in item:
+                key, val = item.split("=", 1)
+                kv[key.strip()] = val.strip()
     if kv.get("kernel_digest") != kernel_digest() or kv.get("workload") != workload:
-        return None
+        return {}
+    return kv
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(_recorded_counters(workload)["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_mfma_utilisation(workload: str):
+    """MFMA busy fraction and SCLK (GHz) from the committed counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles of all SIMDs, and
+    GRBM_GUI_ACTIVE over the kernel time), or None."""
+    kv = _recorded_counters(workload)
+    try:
+        return {"mfma_busy": float(kv["mfma_busy_frac_at_measured_clock"]),
+                "sclk_ghz": float(kv["sclk_from_GRBM_GUI_ACTIVE_GHz"]),
+                "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
     except (KeyError, ValueError):
         return None
 
@@ -637,6 +658,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": recorded_traffic(w.name),
+                     "counters": recorded_mfma_utilisation(w.name),
                      "kernel_ms_avg": round(avg_ms, 4), "kernel_ms_min": round(min(launch_ms), 4),
                      "kernel_digest": kernel_digest()},
     }
