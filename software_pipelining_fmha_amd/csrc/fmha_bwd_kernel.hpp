@@ -404,16 +404,19 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
       floatx4 nl[4];
       stats(cur, 1, nl);
       const int q_s = q_begin + t * T::BS;
+      // Masked scores become -inf (weight 0), on edge steps only: the test
+      // is uniform, so other steps branch past it.
       const bool edge = (CAUSAL && q_s < kw0 + T::RW - 1) || q_s + T::BS > N || kw0 + T::RW > N;
+      if (edge) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nl[i >> 2][i & 3]));
-        if (edge) {
+        for (int i = 0; i < 16; ++i) {
           const int q = q_s + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if ((CAUSAL && q < key) || q >= N || key >= N) pv = 0.f;
+          if ((CAUSAL && q < key) || q >= N || key >= N) sc[i] = -INFINITY;
         }
-        w16[i >> 3][i & 7] = (_Float16)pv;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        w16[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nl[i >> 2][i & 3]));
       *(__attribute__((address_space(3))) half8*)(pbuf + 16 * lane) = w16[0];
       *(__attribute__((address_space(3))) half8*)(pbuf + 1024 + 16 * lane) = w16[1];
     } else {
@@ -657,17 +660,24 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sk + o), qf[k], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sv + o), dof[k], dp[kb], 0, 0, 0);
       }
+    // Masked scores become -inf (weight 0), on edge steps only: the test is
+    // uniform, so other steps branch past it.
     const bool edge = (CAUSAL && k_s + T::BS - 1 > qw0) || k_s + T::BS > N;
+    if (edge) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = k_s + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
+          if ((CAUSAL && kk > qrow) || kk >= N) s[kb][i] = -INFINITY;
+        }
+    }
     half8 dsf[2 * T::KB];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, nl2));
-        if (edge) {
-          const int kk = k_s + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if ((CAUSAL && kk > qrow) || kk >= N) pv = 0.f;
-        }
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, nl2));
         dsf[2 * kb + (i >> 3)][i & 7] = (_Float16)(pv * (dp[kb][i] - Dq));
       }
     // dQ^T += K^T dS^T (k = keys, 16 per k-step)
