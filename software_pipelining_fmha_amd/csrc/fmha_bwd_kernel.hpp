@@ -221,7 +221,7 @@ __device__ __forceinline__ int bwd_tile_id(int G) {
 // k0 + 32 (w % 4). Wave w (the P wave) holds K and forms S = Q K^T, P and
 // dV^T += dO^T P; wave w + 4 (the dS wave) holds V and forms dP = dO V^T,
 // dS = P (dP - D) and dK^T += Q^T dS, taking P from the P wave through LDS.
-// Each step (32 queries) has two barrier-separated intervals in which one
+// Each step (64 queries) has two barrier-separated intervals in which one
 // wave of each SIMD feeds the matrix core while the other runs vector work:
 //   interval A_t: P wave  MFMA  dV_{t-1}, S_t     | dS wave VALU dS_{t-1}
 //   interval B_t: P wave  VALU  P_t (to LDS)      | dS wave MFMA dK_{t-1}, dP_t
@@ -234,7 +234,9 @@ struct DkdvTile {
   static constexpr int PAIRS = 4;
   static constexpr int RW = 32;                  // keys per wave pair
   static constexpr int BT = PAIRS * RW;          // keys per workgroup
-  static constexpr int BS = 32;                  // queries per step
+  static constexpr int BS = 64;                  // queries per step
+  static constexpr int QB = BS / 32;             // 32-query blocks per step
+  static constexpr int QSTEPS = BS / 16;         // MFMA k-steps over a step's queries
   static constexpr int KSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   static constexpr int CPR = D / 8;
@@ -243,9 +245,13 @@ struct DkdvTile {
   static constexpr int STAT_BYTES = 2 * BS * 4;
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES + STAT_BYTES;
   static constexpr int SLOTS = 3;
-  static constexpr int P_BYTES = 2 * 1024;       // one pair's P (32 x 32 fp16)
+  static constexpr int P_BYTES = QSTEPS * 1024;  // one pair's P (64 x 32 fp16)
   static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES + PAIRS * P_BYTES;
-  static_assert(TILE_CHUNKS * 2 == THREADS || TILE_CHUNKS == THREADS, "staging covers a step");
+  // staging: CPT 16-byte chunks per thread for each of the two tiles
+  static constexpr int CPT = TILE_CHUNKS / THREADS;
+  static_assert(CPT >= 1 && CPT * THREADS == TILE_CHUNKS, "staging covers a step");
+  static_assert(2 * BS <= THREADS, "one thread per statistic");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
 };
 
 template <int D, bool CAUSAL>
@@ -299,33 +305,32 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
   off.init(lane);
   const float c2 = p.scale_log2;
 
-  // staging of one step: Q and dO rows (one 16-byte chunk per thread and
-  // tile at d = 128; at d = 64 the first half of the threads takes Q, the
-  // second dO) and the D and -lse*log2(e) values of its 32 queries
-  constexpr bool ONE_EACH = T::TILE_CHUNKS == T::THREADS;
-  const int chunk = ONE_EACH ? tid : tid % T::TILE_CHUNKS;
-  const int crow = chunk / T::CPR, ccol = chunk % T::CPR;
-  const int g_off = (crow * D + 8 * ccol) * 2;
-  const int l_off = crow * D * 2 + 16 * (ccol ^ bwd_swz<D>(crow));
-  const bool stage_q = ONE_EACH || tid < T::TILE_CHUNKS;
-  intx4 sa, sb;
+  // staging of one step: CPT 16-byte chunks per thread of each of the Q and
+  // dO tiles, and the D and -lse*log2(e) values of its BS queries
+  int g_off[T::CPT], l_off[T::CPT];
+#pragma unroll
+  for (int c = 0; c < T::CPT; ++c) {
+    const int chunk = tid + T::THREADS * c;
+    const int crow = chunk / T::CPR, ccol = chunk % T::CPR;
+    g_off[c] = (crow * D + 8 * ccol) * 2;
+    l_off[c] = crow * D * 2 + 16 * (ccol ^ bwd_swz<D>(crow));
+  }
+  intx4 sa[T::CPT], sb[T::CPT];
   float sst = 0.f;
   auto stage_load = [&](int q_s) __attribute__((always_inline)) {
-    if (ONE_EACH) {
-      sa = load16(rq, q_s * D * 2 + g_off);
-      sb = load16(rdo, q_s * D * 2 + g_off);
-    } else {
-      sa = load16(stage_q ? rq : rdo, q_s * D * 2 + g_off);
+#pragma unroll
+    for (int c = 0; c < T::CPT; ++c) {
+      sa[c] = load16(rq, q_s * D * 2 + g_off[c]);
+      sb[c] = load16(rdo, q_s * D * 2 + g_off[c]);
     }
     if (tid < 2 * T::BS)
       sst = tid < T::BS ? load_f32(rD, (q_s + tid) * 4) : load_f32(rL, (q_s + tid - T::BS) * 4);
   };
   auto stage_store = [&](lds_char* sl) __attribute__((always_inline)) {
-    if (ONE_EACH) {
-      *(lds_intx4*)(sl + l_off) = sa;
-      *(lds_intx4*)(sl + T::TILE_BYTES + l_off) = sb;
-    } else {
-      *(lds_intx4*)(sl + (stage_q ? 0 : T::TILE_BYTES) + l_off) = sa;
+#pragma unroll
+    for (int c = 0; c < T::CPT; ++c) {
+      *(lds_intx4*)(sl + l_off[c]) = sa[c];
+      *(lds_intx4*)(sl + T::TILE_BYTES + l_off[c]) = sb[c];
     }
     if (tid < 2 * T::BS) *(__attribute__((address_space(3))) float*)(sl + 2 * T::TILE_BYTES + 4 * tid) = sst;
   };
@@ -337,32 +342,40 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
   auto active = [&](int step) __attribute__((always_inline)) {
     return step >= 0 && step < n_steps && (!CAUSAL || q_begin + step * T::BS + T::BS - 1 >= kw0);
   };
-  auto stats = [&](const lds_char* sl, int which, floatx4 (&v)[4]) __attribute__((always_inline)) {
-    const lds_char* st = sl + 2 * T::TILE_BYTES + which * T::BS * 4;
+  // per-query statistic `which` (0: D, 1: -lse*log2(e)) of query block qb,
+  // as laid out in the accumulators: v[g][e] for register 4 g + e
+  auto stats = [&](const lds_char* sl, int which, int qb, floatx4 (&v)[4]) __attribute__((always_inline)) {
+    const lds_char* st = sl + 2 * T::TILE_BYTES + which * T::BS * 4 + qb * 32 * 4;
 #pragma unroll
     for (int g = 0; g < 4; ++g) v[g] = *(const lds_floatx4*)(st + 4 * (16 * (g >> 1) + 8 * hh + 4 * (g & 1)));
   };
 
-  floatx16 sc;     // S (P wave) or dP (dS wave) of the newest step
-  half8 w16[2];    // P (P wave) or dS (dS wave) of the previous step, fp16
+  // S (P wave) or dP (dS wave) of the newest step, per 32-query block: lane
+  // = key, register i = query 32 qb + 16 (i / 8) + 8 hh + i % 8 of the step
+  floatx16 sc[T::QB];
+  // P (P wave) or dS (dS wave) of the previous step in fp16, per 16-query
+  // k-step: w16[2 qb + i / 8][i % 8] is register i of block qb
+  half8 w16[T::QSTEPS];
 
-  // Matrix-core interval: acc += (tile ct of step t-1)^T w16, then
-  // sc = (tile rt of step t) bf, 2 * DBLK + KSTEPS MFMAs in a fixed order,
-  // each LDS operand read OPERAND_AHEAD MFMAs before its use. It always runs
-  // whole: w16 is zero when step t-1 contributes nothing (the ring starts
-  // zeroed, so its operands are finite), and sc is simply unused when step t
-  // is inactive.
+  // Matrix-core interval: acc += (tile ct of step t-1)^T w16 (DBLK x QSTEPS
+  // MFMAs), then sc = (tile rt of step t) bf (QB x KSTEPS), in a fixed order
+  // in which consecutive MFMAs of one kind alternate accumulators, each LDS
+  // operand read OPERAND_AHEAD MFMAs before its use. It always runs whole:
+  // w16 is zero when step t-1 contributes nothing (the ring starts zeroed, so
+  // its operands are finite), and sc is simply unused when step t is
+  // inactive.
   auto mfma_interval = [&](const lds_char* cs, int ct, const lds_char* rs, int rt)
       __attribute__((always_inline)) {
-    constexpr int NC = 2 * T::DBLK, NM = NC + T::KSTEPS, AHEAD = OPERAND_AHEAD;
+    constexpr int NC = T::DBLK * T::QSTEPS, NM = NC + T::QB * T::KSTEPS, AHEAD = OPERAND_AHEAD;
     const lds_char* csrc = cs + ct * T::TILE_BYTES;
     const lds_char* rsrc = rs + rt * T::TILE_BYTES;
     auto operand = [&](int i) __attribute__((always_inline)) {
       if (i < NC) {
-        const int b = i >> 1, ks = i & 1;
+        const int b = i % T::DBLK, ks = i / T::DBLK;
         return tr_pair(csrc, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
       }
-      return *(const lds_half8*)(rsrc + off.nat[i - NC]);
+      const int n = i - NC, qb = n % T::QB, k = n / T::QB;
+      return *(const lds_half8*)(rsrc + off.nat[k] + qb * 32 * D * 2);
     };
     half8 ring[AHEAD];
 #pragma unroll
@@ -373,17 +386,21 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
       const half8 a = ring[i % AHEAD];
       if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
       if (i < NC) {
-        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w16[i & 1], acc[i >> 1], 0, 0, 0);
+        const int b = i % T::DBLK, ks = i / T::DBLK;
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w16[ks], acc[b], 0, 0, 0);
       } else {
-        const floatx16 c = i == NC ? floatx16{} : sc;
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bf[i - NC], c, 0, 0, 0);
+        const int n = i - NC, qb = n % T::QB, k = n / T::QB;
+        const floatx16 c = k == 0 ? floatx16{} : sc[qb];
+        sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bf[k], c, 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   auto zero_w16 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w16[0][i] = w16[1][i] = (_Float16)0.f;
+    for (int k = 0; k < T::QSTEPS; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w16[k][i] = (_Float16)0.f;
   };
 
   // One step t in the role of this wave. Slot indices are compile-time (U is
@@ -401,24 +418,31 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
     __syncthreads();
     // interval B: P = 2^(S c - lse log2 e) in fp16, to registers and LDS
     if (active(t)) {
-      floatx4 nl[4];
-      stats(cur, 1, nl);
       const int q_s = q_begin + t * T::BS;
       // Masked scores become -inf (weight 0), on edge steps only: the test
       // is uniform, so other steps branch past it.
       const bool edge = (CAUSAL && q_s < kw0 + T::RW - 1) || q_s + T::BS > N || kw0 + T::RW > N;
       if (edge) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q_s + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if ((CAUSAL && q < key) || q >= N || key >= N) sc[i] = -INFINITY;
-        }
+        for (int qb = 0; qb < T::QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = q_s + 32 * qb + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if ((CAUSAL && q < key) || q >= N || key >= N) sc[qb][i] = -INFINITY;
+          }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        w16[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, nl[i >> 2][i & 3]));
-      *(__attribute__((address_space(3))) half8*)(pbuf + 16 * lane) = w16[0];
-      *(__attribute__((address_space(3))) half8*)(pbuf + 1024 + 16 * lane) = w16[1];
+      for (int qb = 0; qb < T::QB; ++qb) {
+        floatx4 nl[4];
+        stats(cur, 1, qb, nl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          w16[2 * qb + (i >> 3)][i & 7] =
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][i], c2, nl[i >> 2][i & 3]));
+      }
+#pragma unroll
+      for (int k = 0; k < T::QSTEPS; ++k)
+        *(__attribute__((address_space(3))) half8*)(pbuf + 1024 * k + 16 * lane) = w16[k];
     } else {
       zero_w16();
     }
@@ -433,14 +457,17 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
     if (t + 1 < n_steps) stage_load(q_begin + (t + 1) * T::BS);
     // interval A: dS = P (dP - D) of step t-1, P from the P wave
     if (active(t - 1)) {
-      floatx4 dd[4];
-      stats(prev, 0, dd);
-      const half8 p0 = *(const lds_half8*)(pbuf + 16 * lane);
-      const half8 p1 = *(const lds_half8*)(pbuf + 1024 + 16 * lane);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
-        w16[i >> 3][i & 7] = (_Float16)(pv * (sc[i] - dd[i >> 2][i & 3]));
+      for (int qb = 0; qb < T::QB; ++qb) {
+        floatx4 dd[4];
+        stats(prev, 0, qb, dd);
+        const half8 p0 = *(const lds_half8*)(pbuf + 1024 * (2 * qb) + 16 * lane);
+        const half8 p1 = *(const lds_half8*)(pbuf + 1024 * (2 * qb + 1) + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+          w16[2 * qb + (i >> 3)][i & 7] = (_Float16)(pv * (sc[qb][i] - dd[i >> 2][i & 3]));
+        }
       }
     } else {
       zero_w16();
