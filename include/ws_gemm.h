@@ -132,7 +132,8 @@ void ws_model_default(ws_model_params *p, int cus);
 
 /* ws_gemm_choose - the compiled variant with the smallest predicted
  * launch time for (M, N, K) under *p (NULL = ws_model_default for the
- * current device). Returns 0, or an fmha.h status code. */
+ * current device); of equal predictions (relative 1e-9) for one tile shape,
+ * the deepest ring. Returns 0, or an fmha.h status code. */
 int ws_gemm_choose(const ws_model_params *p, int M, int N, int K, int *tile_m, int *tile_n,
                    int *tile_k, int *ring);
 
