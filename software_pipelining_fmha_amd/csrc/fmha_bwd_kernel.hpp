@@ -54,22 +54,12 @@ struct BwdParams {
   float scale;
 };
 
+// Sizes shared by the two streaming kernels.
 template <int D>
 struct BwdTile {
-  static constexpr int WAVES = 4;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int RW = 32;             // rows (keys or queries) a wave owns
-  static constexpr int BT = WAVES * RW;     // rows a workgroup owns
-  static constexpr int BS = 32;             // rows streamed per step
+  static constexpr int BT = 128;            // rows (keys or queries) a workgroup owns
   static constexpr int KSTEPS = D / 16;     // MFMA k-steps over d
   static constexpr int DBLK = D / 32;       // 32-row blocks of d
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BS * D * 2;
-  static constexpr int CPL = TILE_BYTES / 16 / THREADS;  // chunks per lane per tile
-  static constexpr int STAT_BYTES = 2 * BS * 4;
-  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + STAT_BYTES;
-  static constexpr int LDS_BYTES = 2 * SLOT_BYTES;
-  static_assert(CPL >= 1 && CPL * 16 * THREADS == TILE_BYTES, "staging covers a tile");
 };
 
 // Chunk swizzle of the streamed tiles. For D = 128 (256-byte rows) it is a
@@ -118,54 +108,6 @@ __global__ __launch_bounds__(256) void fmha_bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Shared pieces of the two streaming kernels
 // ---------------------------------------------------------------------------
-template <int D>
-struct Stream {
-  using T = BwdTile<D>;
-  typedef __attribute__((address_space(3))) char lds_char;
-  typedef __attribute__((address_space(3))) half8 lds_half8;
-  typedef __attribute__((address_space(3))) intx4 lds_intx4;
-  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
-
-  // Staging of one step: two [BS][D] fp16 tiles (rows r0 .. r0+BS-1 of a and
-  // b) and BS values of each of two per-row statistics.
-  intx4 ra[T::CPL], rb[T::CPL];
-  float rs;
-  int g_off[T::CPL], l_off[T::CPL];
-
-  __device__ __forceinline__ void init(int tid) {
-#pragma unroll
-    for (int i = 0; i < T::CPL; ++i) {
-      const int x = tid + T::THREADS * i;
-      const int row = x / T::CPR, c = x % T::CPR;
-      g_off[i] = (row * D + 8 * c) * 2;
-      l_off[i] = row * D * 2 + 16 * (c ^ bwd_swz<D>(row));
-    }
-  }
-  template <bool STATS>
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t a, __amdgpu_buffer_rsrc_t b,
-                                       __amdgpu_buffer_rsrc_t s0, __amdgpu_buffer_rsrc_t s1,
-                                       int r0, int tid) {
-#pragma unroll
-    for (int i = 0; i < T::CPL; ++i) {
-      ra[i] = load16(a, r0 * D * 2 + g_off[i]);
-      rb[i] = load16(b, r0 * D * 2 + g_off[i]);
-    }
-    if (STATS && tid < 2 * T::BS)
-      rs = tid < T::BS ? load_f32(s0, (r0 + tid) * 4) : load_f32(s1, (r0 + tid - T::BS) * 4);
-  }
-  template <bool STATS>
-  __device__ __forceinline__ void store(lds_char* slot, int tid) {
-#pragma unroll
-    for (int i = 0; i < T::CPL; ++i) {
-      *(lds_intx4*)(slot + l_off[i]) = ra[i];
-      *(lds_intx4*)(slot + T::TILE_BYTES + l_off[i]) = rb[i];
-    }
-    if (STATS && tid < 2 * T::BS)
-      *(__attribute__((address_space(3))) float*)(slot + 2 * T::TILE_BYTES + 4 * tid) = rs;
-  }
-};
-
 // Transposed A operand (8 rows of one d column per lane) from two
 // ds_read_b64_tr_b16 reads.
 __device__ __forceinline__ half8 tr_pair(const __attribute__((address_space(3))) char* base, int off0,
