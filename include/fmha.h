@@ -30,7 +30,7 @@ extern "C" {
 /* Status codes returned by fmha_fwd. */
 #define FMHA_OK 0
 #define FMHA_ERR_INVALID_ARGUMENT 1 /* null pointer, negative size, non-finite scale, aliasing outputs */
-#define FMHA_ERR_UNSUPPORTED 2      /* head dim, scale sign, alignment or size outside what the kernel handles */
+#define FMHA_ERR_UNSUPPORTED 2      /* head dim, alignment, size or descale outside what the kernels handle */
 #define FMHA_ERR_HIP 3              /* the kernel launch itself failed */
 
 /*
@@ -48,8 +48,9 @@ extern "C" {
  * d       : head dimension, 64 or 128.
  * causal  : non-zero means key j is visible to query i only if j <= i (square,
  *           top-left aligned). Zero means every key is visible.
- * scale   : multiplier on q.k before the softmax; finite and > 0 (the usual
- *           value is 1/sqrt(d)).
+ * scale   : multiplier on q.k before the softmax; any finite value (the usual
+ *           value is 1/sqrt(d); 0 gives uniform weights over the visible
+ *           keys, a negative value favours the smallest q.k).
  * stream  : hipStream_t to enqueue on (NULL = the default stream).
  *
  * Ownership. All five buffers are caller-owned device memory on the current

@@ -291,7 +291,7 @@ static void row_stats(const head_args_t *a, int64_t head, int64_t i, double *s, 
 /* dq_i of one query row, from the definition. s is scratch of N doubles.
  * If rss is not NULL it receives, per element, sqrt(sum_j (scale dS_ij k_jc)^2):
  * the root-sum-square of the terms (a tolerance scale for callers). If dsens
- * is not NULL it receives scale * w_i * sum_j P_ij |k_jc|, the bound on how
+ * is not NULL it receives |scale| * w_i * sum_j P_ij |k_jc|, the bound on how
  * dq_i moves per unit relative error in o_i through D_i. */
 static void dq_row(const head_args_t *a, int64_t head, int64_t i, double *s, double *od,
                    double *dq, double *rss, double *dsens)
@@ -330,16 +330,16 @@ static void dq_row(const head_args_t *a, int64_t head, int64_t i, double *s, dou
         dq[c] *= a->scale;
     if (rss)
         for (int64_t c = 0; c < d; ++c)
-            rss[c] = a->scale * sqrt(rss[c]);
+            rss[c] = fabs(a->scale) * sqrt(rss[c]);
     if (dsens)
         for (int64_t c = 0; c < d; ++c)
-            dsens[c] *= a->scale * w;
+            dsens[c] *= fabs(a->scale) * w;
 }
 
 /* dk_j and dv_j of one key row. lse, D and W hold the row statistics of
  * every query row of the head. If rk / rv are not NULL they receive the
  * root-sum-square of the terms of each element, as in dq_row; if dsk is not
- * NULL it receives scale * sqrt(sum_i (P_ij w_i q_ic)^2), the root-sum-square
+ * NULL it receives |scale| * sqrt(sum_i (P_ij w_i q_ic)^2), the root-sum-square
  * of the per-query D sensitivities of dk_j. */
 static void dkdv_row(const head_args_t *a, int64_t head, int64_t j, const double *lse,
                      const double *D, const double *W, double *dk, double *dv, double *rk,
@@ -383,12 +383,12 @@ static void dkdv_row(const head_args_t *a, int64_t head, int64_t j, const double
         dk[c] *= a->scale;
     if (rk)
         for (int64_t c = 0; c < d; ++c) {
-            rk[c] = a->scale * sqrt(rk[c]);
+            rk[c] = fabs(a->scale) * sqrt(rk[c]);
             rv[c] = sqrt(rv[c]);
         }
     if (dsk)
         for (int64_t c = 0; c < d; ++c)
-            dsk[c] = a->scale * sqrt(dsk[c]);
+            dsk[c] = fabs(a->scale) * sqrt(dsk[c]);
 }
 
 typedef struct {
@@ -647,7 +647,7 @@ static void build_e4m3_table(void)
  * normal range): with e_j = max(2^-4 P_ij, 2^-10 P_max),
  *   rss_o[c] = sqrt(sum_j e_j^2 (v_jc - o_c)^2),  rss_l = sqrt(sum_j e_j^2);
  * and sc_o / sc_l a scale for errors in the scores proportional to
- * a_j = scale * sum_c |q_c k_jc| (the sum of the magnitudes of the products):
+ * a_j = |scale| * sum_c |q_c k_jc| (the sum of the magnitudes of the products):
  *   sc_o[c] = sum_j P_ij a_j |v_jc - o_c|,  sc_l = sum_j P_ij a_j. */
 static void one_row_fp8(const f8job_t *jb, int64_t r, double *s)
 {
@@ -718,7 +718,7 @@ static void one_row_fp8(const f8job_t *jb, int64_t r, double *s)
             double a = 0.0;
             for (int64_t c = 0; c < d; ++c)
                 a += fabs((jb->dq * g_e4m3[qi[c]]) * (jb->dk * g_e4m3[kj[c]]));
-            a *= jb->scale;
+            a *= fabs(jb->scale);
             sl += P * a;
             for (int64_t c = 0; c < d; ++c)
                 so[c] += P * a * fabs(jb->dv * g_e4m3[vj[c]] - o[c]);

@@ -53,8 +53,12 @@ int launch(const fmha::Params& prm, hipStream_t stream) {
   return e == hipSuccess ? FMHA_OK : FMHA_ERR_HIP;
 }
 
-template <int D>
-int tile_rows() { return fmha::Tile<D>::BM; }
+// Sign of a finite scale (-0 counts as 0) and the magnitude the forward
+// kernels multiply by (1 for scale = 0, where Q is zeroed instead).
+int scale_sign(float scale) { return scale > 0.f ? 1 : (scale < 0.f ? -1 : 0); }
+double scale_magnitude(float scale) {
+  return scale == 0.f ? 1.0 : std::fabs(static_cast<double>(scale));
+}
 
 }  // namespace
 
@@ -76,7 +80,6 @@ extern "C" int fmha_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (B == 0 || H == 0 || N == 0) return FMHA_OK;  // empty: nothing to do, pointers unused
   if (!q || !k || !v || !o || !lse) return FMHA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f)) return FMHA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FMHA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FMHA_ERR_UNSUPPORTED;
@@ -104,7 +107,10 @@ extern "C" int fmha_fwd(const void* q, const void* k, const void* v, void* o, fl
   prm.N = N;
   prm.n_qt = static_cast<int>(n_qt);
   prm.total_wg = static_cast<int>(grid);
-  prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  // the kernel multiplies by |scale| and folds the sign into Q (scale = 0:
+  // Q becomes 0 and any positive multiplier gives the same zero scores)
+  prm.q_sign = scale_sign(scale);
+  prm.scale_log2 = static_cast<float>(scale_magnitude(scale) * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 64) return causal ? launch<64, true>(prm, s) : launch<64, false>(prm, s);
@@ -138,26 +144,27 @@ extern "C" size_t fmha_bwd_workspace_bytes(int B, int H, int N) {
   return static_cast<size_t>(2) * B * H * N * sizeof(float);
 }
 
-extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H,
-                        int N, int d, int causal, float scale, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return FMHA_ERR_INVALID_ARGUMENT;
-  if (B == 0 || H == 0 || N == 0) return FMHA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws)
-    return FMHA_ERR_INVALID_ARGUMENT;
+namespace fmha_host {
+
+// Argument checks of the backward pass, shared by the entry points that take
+// a workspace and that bring their own. ws is not examined here.
+__attribute__((visibility("hidden"))) int check_bwd(const void* q, const void* k, const void* v,
+                                                    const void* o, const void* dout,
+                                                    const float* lse, void* dq, void* dk,
+                                                    void* dv, int B, int H, int N, int d,
+                                                    float scale) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FMHA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return FMHA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f)) return FMHA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FMHA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(ws, 4))
+      !aligned(lse, 4))
     return FMHA_ERR_UNSUPPORTED;
   if ((static_cast<int64_t>(N) + 256) * d * 2 >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
   const int64_t rows = static_cast<int64_t>(B) * H * N;
   if (rows >= (int64_t(1) << 30)) return FMHA_ERR_UNSUPPORTED;
   const int bt = fmha::BwdTile<128>::BT;
-  const int64_t n_t = (N + bt - 1) / bt;
-  const int64_t grid = static_cast<int64_t>(B) * H * n_t;
+  const int64_t grid = static_cast<int64_t>(B) * H * ((N + bt - 1) / bt);
   if (grid >= (int64_t(1) << 31)) return FMHA_ERR_UNSUPPORTED;
 
   const uint64_t tb = static_cast<uint64_t>(rows) * d * 2;
@@ -167,14 +174,22 @@ extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void*
   for (void* out : outs) {
     for (const void* in : ins)
       if (overlap(out, tb, in, tb)) return FMHA_ERR_INVALID_ARGUMENT;
-    if (overlap(out, tb, lse, lb) || overlap(out, tb, ws, 2 * lb)) return FMHA_ERR_INVALID_ARGUMENT;
+    if (overlap(out, tb, lse, lb)) return FMHA_ERR_INVALID_ARGUMENT;
     for (void* other : outs)
       if (other != out && overlap(out, tb, other, tb)) return FMHA_ERR_INVALID_ARGUMENT;
   }
-  for (const void* in : ins)
-    if (overlap(ws, 2 * lb, in, tb)) return FMHA_ERR_INVALID_ARGUMENT;
-  if (overlap(ws, 2 * lb, lse, lb)) return FMHA_ERR_INVALID_ARGUMENT;
+  return FMHA_OK;
+}
 
+// The three launches, after the checks, with ws of 2 * B*H*N floats.
+__attribute__((visibility("hidden"))) int run_bwd(const void* q, const void* k, const void* v,
+                                                  const void* o, const void* dout,
+                                                  const float* lse, void* dq, void* dk, void* dv,
+                                                  float* ws, int B, int H, int N, int d,
+                                                  int causal, float scale, void* stream) {
+  const int64_t rows = static_cast<int64_t>(B) * H * N;
+  const int bt = fmha::BwdTile<128>::BT;
+  const int64_t n_t = (N + bt - 1) / bt;
   fmha::BwdParams prm;
   prm.q = static_cast<const _Float16*>(q);
   prm.k = static_cast<const _Float16*>(k);
@@ -189,13 +204,36 @@ extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void*
   prm.N = N;
   prm.rows = static_cast<int>(rows);
   prm.n_t = static_cast<int>(n_t);
-  prm.total_wg = static_cast<int>(grid);
+  prm.total_wg = static_cast<int>(static_cast<int64_t>(B) * H * n_t);
   prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   prm.scale = scale;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d == 64) return causal ? launch_bwd<64, true>(prm, s) : launch_bwd<64, false>(prm, s);
   return causal ? launch_bwd<128, true>(prm, s) : launch_bwd<128, false>(prm, s);
+}
+
+}  // namespace fmha_host
+
+using fmha_host::check_bwd;
+using fmha_host::run_bwd;
+
+extern "C" int fmha_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, float* ws, int B, int H,
+                        int N, int d, int causal, float scale, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FMHA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || H == 0 || N == 0) return FMHA_OK;
+  if (!ws) return FMHA_ERR_INVALID_ARGUMENT;
+  const int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale);
+  if (st != FMHA_OK) return st;
+  if (!aligned(ws, 4)) return FMHA_ERR_UNSUPPORTED;
+  const uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  const uint64_t tb = rows * d * 2, lb = rows * 4;
+  const void* bufs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* b : bufs)
+    if (overlap(ws, 2 * lb, b, tb)) return FMHA_ERR_INVALID_ARGUMENT;
+  if (overlap(ws, 2 * lb, lse, lb)) return FMHA_ERR_INVALID_ARGUMENT;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, causal, scale, stream);
 }
 
 extern "C" int fmha_fwd_fp8(const void* q, const void* k, const void* v, float descale_q,
@@ -207,8 +245,7 @@ extern "C" int fmha_fwd_fp8(const void* q, const void* k, const void* v, float d
   if (!std::isfinite(scale) || !std::isfinite(descale_q) || !std::isfinite(descale_k) ||
       !std::isfinite(descale_v))
     return FMHA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f) || !(descale_q > 0.f) || !(descale_k > 0.f) || !(descale_v > 0.f))
-    return FMHA_ERR_UNSUPPORTED;
+  if (!(descale_q > 0.f) || !(descale_k > 0.f) || !(descale_v > 0.f)) return FMHA_ERR_UNSUPPORTED;
   if (d != fmha::Fp8Tile::D) return FMHA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FMHA_ERR_UNSUPPORTED;
@@ -232,9 +269,12 @@ extern "C" int fmha_fwd_fp8(const void* q, const void* k, const void* v, float d
   prm.N = N;
   prm.n_qt = static_cast<int>(n_qt);
   prm.total_wg = static_cast<int>(grid);
-  prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * descale_q * descale_k *
+  prm.scale_log2 = static_cast<float>(scale_magnitude(scale) * descale_q * descale_k *
                                       1.4426950408889634);
   prm.descale_v = descale_v;
+  const int sign = scale_sign(scale);
+  prm.q_and = sign == 0 ? 0u : 0xffffffffu;
+  prm.q_xor = sign < 0 ? 0x80808080u : 0u;
   void* args[] = {&prm};
   const void* fn = causal ? reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<true>)
                           : reinterpret_cast<const void*>(&fmha::fmha_fwd_fp8_kernel<false>);
@@ -250,7 +290,7 @@ extern "C" const char* fmha_status_str(int status) {
   switch (status) {
     case FMHA_OK: return "ok";
     case FMHA_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case FMHA_ERR_UNSUPPORTED: return "unsupported shape, alignment or scale";
+    case FMHA_ERR_UNSUPPORTED: return "unsupported head dim, alignment, size or descale";
     case FMHA_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }

@@ -50,7 +50,7 @@ struct BwdParams {
   int rows;          // B * H * N
   int n_t;           // 128-row tiles per head
   int total_wg;      // B * H * n_t
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e) (any sign: masks apply after scaling)
   float scale;
 };
 
@@ -361,7 +361,15 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
     // interval B: P = 2^(S c - lse log2 e) in fp16, to registers and LDS
     if (active(t)) {
       const int q_s = q_begin + t * T::BS;
-      // Masked scores become -inf (weight 0), on edge steps only: the test
+      // base-2 exponents s c - lse log2 e (any finite scale)
+#pragma unroll
+      for (int qb = 0; qb < T::QB; ++qb) {
+        floatx4 nl[4];
+        stats(cur, 1, qb, nl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[qb][i] = __builtin_fmaf(sc[qb][i], c2, nl[i >> 2][i & 3]);
+      }
+      // Masked exponents become -inf (weight 0), on edge steps only: the test
       // is uniform, so other steps branch past it.
       const bool edge = (CAUSAL && q_s < kw0 + T::RW - 1) || q_s + T::BS > N || kw0 + T::RW > N;
       if (edge) {
@@ -374,14 +382,10 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
           }
       }
 #pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) {
-        floatx4 nl[4];
-        stats(cur, 1, qb, nl);
+      for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          w16[2 * qb + (i >> 3)][i & 7] =
-              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][i], c2, nl[i >> 2][i & 3]));
-      }
+          w16[2 * qb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(sc[qb][i]);
 #pragma unroll
       for (int k = 0; k < T::QSTEPS; ++k)
         *(__attribute__((address_space(3))) half8*)(pbuf + 1024 * k + 16 * lane) = w16[k];
@@ -629,8 +633,13 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sk + o), qf[k], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sv + o), dof[k], dp[kb], 0, 0, 0);
       }
-    // Masked scores become -inf (weight 0), on edge steps only: the test is
-    // uniform, so other steps branch past it.
+    // base-2 exponents s c - lse log2 e (any finite scale)
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_fmaf(s[kb][i], c2, nl2);
+    // Masked exponents become -inf (weight 0), on edge steps only: the test
+    // is uniform, so other steps branch past it.
     const bool edge = (CAUSAL && k_s + T::BS - 1 > qw0) || k_s + T::BS > N;
     if (edge) {
 #pragma unroll
@@ -646,7 +655,7 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, nl2));
+        const float pv = __builtin_amdgcn_exp2f(s[kb][i]);
         dsf[2 * kb + (i >> 3)][i & 7] = (_Float16)(pv * (dp[kb][i] - Dq));
       }
     // dQ^T += K^T dS^T (k = keys, 16 per k-step)

@@ -51,8 +51,12 @@ struct Fp8Params {
   int N;             // sequence length
   int n_qt;          // query tiles per head
   int total_wg;      // B * H * n_qt
-  float scale_log2;  // scale * descale_q * descale_k * log2(e)
+  float scale_log2;  // |scale| * descale_q * descale_k * log2(e) (> 0)
   float descale_v;
+  // The sign of scale, folded into the Q bytes (E4M3 negation flips bit 7,
+  // zero clears the byte; both exact): byte = (byte & q_and) ^ q_xor.
+  uint32_t q_and;    // 0xffffffff, or 0 for scale = 0
+  uint32_t q_xor;    // 0x80808080 for scale < 0, else 0
 };
 
 struct Fp8Tile {
@@ -131,6 +135,13 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     const intx4 a = load16(rq, qrow * D + 64 * s + 32 * hh);
     const intx4 b = load16(rq, qrow * D + 64 * s + 32 * hh + 16);
     qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // The C stage needs a positive multiplier, so the sign of scale rides on Q.
+  if (p.q_and != 0xffffffffu || p.q_xor != 0u) {
+#pragma unroll
+    for (int s = 0; s < T::KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = (int)(((uint32_t)qf[s][e] & p.q_and) ^ p.q_xor);
   }
 
   floatx16 oacc[T::DBLK];

@@ -69,7 +69,8 @@ struct Params {
   int N;            // sequence length (queries = keys)
   int n_qt;         // query tiles per head
   int total_wg;     // B * H * n_qt
-  float scale_log2; // scale * log2(e): scores go to the base-2 domain
+  float scale_log2; // |scale| * log2(e) (> 0): scores go to the base-2 domain
+  int q_sign;       // sign of scale (1, -1 or 0), folded into the Q operand
 };
 
 template <int D>
@@ -146,13 +147,20 @@ __device__ __forceinline__ int key_of_row(int p) {
   return p ^ (flip * 0xC);
 }
 
-// LDS byte offset of 16-byte chunk c of row p in a K tile. The chunk index is
-// XOR-swizzled with the row, so 16 lanes reading one chunk column of 16
-// consecutive rows hit 16 distinct bank groups.
+// Chunk swizzle of row p of a K tile. 16 lanes reading one chunk column of
+// 16 consecutive rows must hit 16 distinct 4-bank groups of the 64 banks: at
+// d = 128 a row is 256 bytes (every bank once), so the 16 rows need 16
+// distinct chunks; at d = 64 a row is 128 bytes (half the banks, by the
+// row's parity), so each parity's 8 rows need 8 distinct chunks.
+template <int D>
+__device__ __forceinline__ int k_swz(int p) {
+  return D == 128 ? (p & 15) : ((p >> 1) & 7);
+}
+// LDS byte offset of 16-byte chunk c of row p in a K tile.
 template <int D>
 __device__ __forceinline__ int k_chunk_off(int p, int c) {
   constexpr int CPR = D / 8;
-  return (p * CPR + (c ^ (p % CPR))) * 16;
+  return (p * CPR + (c ^ k_swz<D>(p))) * 16;
 }
 
 template <int D, bool CAUSAL>
@@ -195,6 +203,15 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
 #pragma unroll
   for (int s = 0; s < T::KSTEPS; ++s)
     qf[s] = __builtin_bit_cast(half8, load16(rq, (qrow * D + 16 * s + 8 * hh) * 2));
+  // The C stage needs a positive multiplier (its row max is taken on the raw
+  // scores, and masked scores are -inf). So the sign of scale rides on Q,
+  // where multiplying by -1 or 0 is exact: (-q).k * |scale| = q.k * scale,
+  // and scale = 0 gives scores of exactly 0 (uniform weights).
+  if (p.q_sign != 1) {
+    const _Float16 f = (_Float16)(float)p.q_sign;
+#pragma unroll
+    for (int s = 0; s < T::KSTEPS; ++s) qf[s] = qf[s] * f;
+  }
 
   floatx16 oacc[T::DBLK];
 #pragma unroll
@@ -232,7 +249,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   for (int r = 0; r < T::LOADS_PER_WAVE; ++r) {
     const int x = 64 * (wave * T::LOADS_PER_WAVE + r) + lane;  // LDS chunk index
     const int row = x / T::CPR, slot = x % T::CPR;
-    k_src[r] = (key_of_row(row) * D + 8 * (slot ^ (row % T::CPR))) * 2;
+    k_src[r] = (key_of_row(row) * D + 8 * (slot ^ k_swz<D>(row))) * 2;
   }
   auto fetch_k = [&](int j, int slot) __attribute__((always_inline)) {
     lds_char* dst = k_ring + slot * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
@@ -305,8 +322,8 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
 
   // ---- consumer-side LDS offsets (per lane, constant over the loop) ----------
   // QK^T A operand: row 32*kb + l32 of the K tile, chunk 2*s + hh. The
-  // swizzle depends on the row only through row % CPR, so the 32-row block kb
-  // adds a constant.
+  // swizzle depends on the row only through its low 4 bits, so the 32-row
+  // block kb adds a constant.
   int k_rd[T::KSTEPS];
 #pragma unroll
   for (int s = 0; s < T::KSTEPS; ++s) k_rd[s] = k_chunk_off<D>(l32, 2 * s + hh);

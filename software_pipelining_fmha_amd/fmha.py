@@ -221,3 +221,4 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None
     if st != FMHA_OK:
         raise FmhaError(st)
     return dq, dk, dv
+

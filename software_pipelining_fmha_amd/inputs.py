@@ -183,8 +183,18 @@ def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:
     return np.stack([b, h, i], axis=1).astype(np.int64)
 
 
+# Row edges of the FP16 and FP8 forward kernels at head dim 128: a key tile
+# (BN = 64) and a query tile (BM = 256) of a workgroup, plus the 32 query
+# rows of one wave and the 128 rows of one group of four waves. The ABI
+# reports BM and BN (fmha_query_tile, fmha_key_tile); a CPU test checks that
+# they agree with these.
+FWD_KEY_TILE = 64
+FWD_QUERY_TILE = 256
+TILE_EDGES = (32, FWD_KEY_TILE, 128, FWD_QUERY_TILE)
+
+
 def boundary_rows(B: int, H: int, N: int, heads: int, seed: int,
-                  tiles=(64, 128)) -> np.ndarray:
+                  tiles=TILE_EDGES) -> np.ndarray:
     """Rows at tile edges of a few seeded heads: 0, 1, t-1, t for each tile
     size t, and N-1."""
     rng = np.random.default_rng(seed)

@@ -50,9 +50,23 @@ def test_non_finite_scale_is_invalid(scale):
     assert call(scale=scale) == fmha.FMHA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125])
-def test_non_positive_scale_is_unsupported(scale):
-    assert call(scale=scale) == fmha.FMHA_ERR_UNSUPPORTED
+def no_gpu():
+    """True when no GPU is visible: then a call that passes every argument
+    check fails at its first HIP call (status 3) instead of launching on
+    the fake addresses these tests pass."""
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except ImportError:  # pragma: no cover
+        return True
+
+
+@pytest.mark.skipif(not no_gpu(), reason="would launch on fake device addresses")
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.125, -3.0])
+def test_any_finite_scale_passes_the_checks(scale):
+    assert call(scale=scale) == fmha.FMHA_ERR_HIP
+    assert call_fp8(scale=scale) == fmha.FMHA_ERR_HIP
+    assert call_bwd(scale=scale) == fmha.FMHA_ERR_HIP
 
 
 @pytest.mark.parametrize("d", [0, 32, 96, 256, -64])
@@ -106,6 +120,15 @@ def test_tiles_reported():
     assert fmha.fmha_query_tile(96) == 0 and fmha.fmha_key_tile(96) == 0
 
 
+def test_row_sampler_uses_the_kernel_tiles():
+    """The causal workloads' edge rows (inputs.boundary_rows) are taken at the
+    forward kernels' real tile sizes."""
+    from software_pipelining_fmha_amd import inputs
+    assert fmha.fmha_query_tile(128) == inputs.FWD_QUERY_TILE
+    assert fmha.fmha_key_tile(128) == inputs.FWD_KEY_TILE
+    assert {inputs.FWD_QUERY_TILE, inputs.FWD_KEY_TILE} <= set(inputs.TILE_EDGES)
+
+
 def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(fmha, "_lib", None)
     monkeypatch.setattr(fmha, "_LIB_PATH", "/nonexistent/libfmha.so")
@@ -128,8 +151,8 @@ def test_fp8_non_finite_factor_is_invalid(which):
     assert call_fp8(**{which: math.nan}) == fmha.FMHA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("which", ["dq", "dk", "dv", "scale"])
-def test_fp8_non_positive_factor_is_unsupported(which):
+@pytest.mark.parametrize("which", ["dq", "dk", "dv"])
+def test_fp8_non_positive_descale_is_unsupported(which):
     assert call_fp8(**{which: 0.0}) == fmha.FMHA_ERR_UNSUPPORTED
 
 
@@ -145,3 +168,32 @@ def test_fp8_output_aliasing_input_is_invalid():
 
 def test_fp8_empty_problem_is_ok():
     assert call_fp8(B=0) == fmha.FMHA_OK
+
+
+BWD = dict(q=A, k=2 * A, v=3 * A, o=4 * A, dout=5 * A, lse=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+           ws=10 * A)
+
+
+def call_bwd(B=1, H=1, N=128, d=128, causal=0, scale=0.088, **ptrs):
+    p = dict(BWD, **ptrs)
+    return fmha.fmha_bwd(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"], p["dk"],
+                         p["dv"], p["ws"], B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("which", sorted(BWD))
+def test_bwd_null_pointer_is_invalid(which):
+    assert call_bwd(**{which: 0}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("which", ["dq", "dk", "dv", "ws"])
+def test_bwd_output_aliasing_input_is_invalid(which):
+    assert call_bwd(**{which: A}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf])
+def test_bwd_non_finite_scale_is_invalid(scale):
+    assert call_bwd(scale=scale) == fmha.FMHA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_empty_problem_is_ok():
+    assert call_bwd(N=0) == fmha.FMHA_OK

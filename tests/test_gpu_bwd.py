@@ -97,6 +97,18 @@ def test_small_and_ragged_shapes_every_row(B, H, N, d, causal, device):
     check_all_rows(q, k, v, do, causal, np.float32(1 / math.sqrt(d)), "small")
 
 
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
+@pytest.mark.parametrize("scale", [0.0, -0.088388, -0.5])
+def test_zero_and_negative_scale(scale, d, causal, device):
+    """Any finite scale: masks apply after the exponent is scaled, so masked
+    keys keep weight 0 for scale <= 0 too (scale = 0 gives dq = dk = 0)."""
+    B, H, N = 1, 3, 200
+    print("bwd scale=%g d=%d causal=%d" % (scale, d, causal), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=3500 + d + causal)
+    do = inputs.draw_dout(B, H, N, d, seed=3600 + d + causal)
+    check_all_rows(q, k, v, do, causal, np.float32(scale), "scale %g" % scale)
+
+
 @pytest.mark.parametrize("idx", [0, 1], ids=[inputs.WORKLOADS[i].name for i in (0, 1)])
 def test_workload_every_row(idx, device):
     """The tiny workload, and B4 H32 N1024 d128 on 4 of its 128 heads (each

@@ -139,6 +139,49 @@ def test_fp8_uniform_keys_every_row(device):
     assert (err <= E_MFMA * a + 1e-5).all()
 
 
+def test_fp8_mfma_score_error_within_its_term(device):
+    """Pins the bar's MFMA term E = 2^-11 on the kernel itself. Within each
+    head every key row is the same random E4M3 row u, and there is one key
+    tile (N = 64), so every weight is exactly 1 and lse_i - ln N is the
+    kernel's score scale * q_i . u as the FP8 MFMA summed it (plus fp32
+    rounding of lse, covered by the floor). Over 131072 random query rows the
+    error against the exact fp64 score must stay within E * a_i, a_i =
+    scale * sum_c |q_ic u_c|. The measured fraction of the term is printed:
+    the MFMA does not add its 128 products exactly, so the error is far above
+    an fp32 summation's (a probe found 2^-11.9 of a_i at worst)."""
+    B, H, N, d = 16, 128, 64, 128
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6868)
+    q8, k8, v8 = (np.array(x) for x in b)
+    k8[:] = k8[:, :, :1]
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run((q8, k8, v8), sc, False, scale)
+    q = oracle.e4m3_to_double(q8) * float(sc[0])
+    u = oracle.e4m3_to_double(k8[:, :, 0]) * float(sc[1])
+    s_ = float(scale) * np.einsum("bhnd,bhd->bhn", q, u)
+    a = float(scale) * np.einsum("bhnd,bhd->bhn", np.abs(q), np.abs(u))
+    err = np.abs(lse.astype(np.float64) - (s_ + math.log(N)))
+    floor = 2.0 ** -20 * np.abs(s_ + math.log(N)) + 2.0 ** -16
+    ratio = err / (E_MFMA * a + floor)
+    worst = float((err / np.maximum(a, 1e-30)).max())
+    print("fp8 MFMA score error: max err/bar %.3f, max err/a = 2^%.2f (fp32 sums: 2^%.1f)" % (
+        ratio.max(), math.log2(worst), math.log2(d * 2.0 ** -24)), flush=True)
+    assert (ratio <= 1).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.0, -0.088388, -0.3])
+def test_fp8_zero_and_negative_scale(scale, causal, device):
+    """Any finite scale: the kernel folds its sign into the Q bytes."""
+    B, H, N, d = 2, 3, 333, 128
+    print("fp8 scale=%g causal=%d" % (scale, causal), flush=True)
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6900 + causal)
+    scale = np.float32(scale)
+    o, lse = run(b, sc, causal, scale)
+    rows = np.argwhere(np.ones((B, H, N), bool))
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 scale %g" % scale)
+
+
 def _quantized(q, k, v):
     """Per-tensor E4M3 quantization of float32 q, k, v."""
     b, sc = zip(*(inputs.quantize_e4m3(x) for x in (q, k, v)))

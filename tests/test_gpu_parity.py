@@ -269,13 +269,40 @@ def test_guard_bands_untouched(device):
     assert np.isfinite(obc[pad:-pad]).all()
 
 
-def test_other_scale_values(device):
-    q, k, v = inputs.draw_qkv(1, 3, 190, 64, seed=16)
-    for scale in (np.float32(0.02), np.float32(0.5)):
-        o, lse = run(q, k, v, True, scale)
-        o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=True, scale=scale)
-        rows = np.argwhere(np.ones((1, 3, 190), bool))
-        check_rows(o, lse, rows, o_ref.reshape(-1, 64), lse_ref.reshape(-1), "scale")
+@pytest.mark.parametrize("d,causal", [(64, True), (64, False), (128, True), (128, False)])
+@pytest.mark.parametrize("scale", [0.02, 0.5, 0.0, -0.0, -0.088388, -0.5])
+def test_other_scale_values(scale, d, causal, device):
+    """Any finite scale: small and large positive ones, zero (uniform weights
+    over the visible keys) and negative ones (the smallest q.k wins)."""
+    N = 190 if d == 64 else 333
+    print("scale=%g d=%d causal=%d" % (scale, d, causal), flush=True)
+    q, k, v = inputs.draw_qkv(1, 3, N, d, seed=16 + d + causal)
+    scale = np.float32(scale)
+    o, lse = run(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
+    rows = np.argwhere(np.ones((1, 3, N), bool))
+    check_rows(o, lse, rows, o_ref.reshape(-1, d), lse_ref.reshape(-1), "scale")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_the_mean_of_visible_values(causal, device):
+    """scale = 0 at a full-size shape with every row checked in closed form:
+    O_i is the mean of the visible value rows and lse_i = ln |J_i|."""
+    B, H, N, d = 4, 32, 2048, 128
+    print("zero scale B=%d H=%d N=%d causal=%d" % (B, H, N, causal), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=808 + causal)
+    o, lse = run(q, k, v, causal, np.float32(0.0))
+    if causal:
+        cnt = np.arange(1, N + 1, dtype=np.float64)
+        mean = np.cumsum(v.astype(np.float64), axis=2) / cnt[None, None, :, None]
+        lse_ref = np.broadcast_to(np.log(cnt)[None, None, :], lse.shape)
+    else:
+        mean = np.broadcast_to(v.astype(np.float64).mean(axis=2, keepdims=True), v.shape)
+        lse_ref = np.full(lse.shape, math.log(N))
+    eo = np.abs(o.astype(np.float64) - mean).max()
+    el = np.abs(lse.astype(np.float64) - lse_ref).max()
+    print("zero scale: max|dO|=%.3e max|dlse|=%.3e" % (eo, el), flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
 
 
 def test_empty_problem_launches_nothing(device):

@@ -51,10 +51,20 @@ def test_sample_rows_distinct_in_range_reproducible():
 
 
 def test_causal_rows_include_tile_edges():
+    """The causal workload checks, in 4 seeded heads, rows 0, 1, BN-1, BN,
+    BM-1, BM and N-1 of the forward kernel's tiles (BN = 64 keys, BM = 256
+    queries), and the wave (32) and wave-group (128) edges."""
     rows = inputs.workload_rows(4)
-    i = set(rows[:, 2].tolist())
-    assert {0, 1, 63, 64, 127, 128, 8191} <= i
-    assert len(rows) >= 256
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 8191}
+    heads = {}
+    for b, h, i in rows.tolist():
+        heads.setdefault((b, h), set()).add(i)
+    full = [hd for hd, ii in heads.items() if edges <= ii]
+    assert len(full) >= 4
+    assert len(rows) >= 256 + 4 * len(edges) - 4
+    for idx in range(len(inputs.FP8_WORKLOADS)):
+        if inputs.FP8_WORKLOADS[idx].causal:
+            assert edges <= set(inputs.fp8_workload_rows(idx)[:, 2].tolist())
 
 
 def test_tiny_oracle_regression_fixture():

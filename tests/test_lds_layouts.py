@@ -1,0 +1,286 @@
+"""CPU models of the LDS layouts the kernels use, restated from the kernel
+sources' index formulas, and checked for three properties:
+
+1. the LDS-DMA fill is a bijection: every element of a K or V tile lands in
+   LDS exactly once;
+2. every read returns, in every lane, the element the matrix-core operand
+   needs (the MFMA operand layouts and the transposing reads are modelled
+   element by element);
+3. the reads and writes are free of LDS bank conflicts under this model of
+   gfx950's LDS: 64 banks of 4 bytes, an access served 256 bytes per pass
+   (16 lanes of a 16-byte access, 32 lanes of an 8-byte one), and a pass
+   without conflicts when no bank is asked for two different words.
+
+The transposing reads are modelled as the hardware returns them: within each
+16-lane group, ds_read_b64_tr_b16 takes 4 fp16 values from each source lane
+s (row s / 4, columns 4 (s % 4) .. +3 of a 4 x 16 block) and gives result
+lane i column i of the 4 rows; ds_read_b64_tr_b8 takes 8 bytes from each
+source lane s (row s / 2, bytes 8 (s % 2) .. +7 of an 8 x 16 block) and gives
+result lane i byte i of the 8 rows.
+The measured SQ_LDS_BANK_CONFLICT of the forward kernel is 0.
+"""
+import numpy as np
+import pytest
+
+BANKS = 64
+
+
+def conflict_free(addrs, width):
+    """addrs: byte address per lane (64 lanes) of a `width`-byte access."""
+    per_pass = 256 // width
+    for p0 in range(0, len(addrs), per_pass):
+        seen = {}
+        for a in addrs[p0:p0 + per_pass]:
+            for w in range(a // 4, (a + width) // 4):
+                b = w % BANKS
+                if seen.get(b, w) != w:
+                    return False
+                seen[b] = w
+    return True
+
+
+def key_of_row(p):
+    """Key held by row p of a forward K tile: bits 2 and 3 of p swapped."""
+    flip = ((p >> 2) ^ (p >> 3)) & 1
+    return p ^ (flip * 0xC)
+
+
+def tr_b16(lds, addrs):
+    """ds_read_b64_tr_b16: lds is an array of fp16 element ids by element
+    index (byte address / 2); returns [64][4] element ids."""
+    src = np.array([lds[a // 2:a // 2 + 4] for a in addrs])  # [64][4]
+    out = np.empty((64, 4), dtype=lds.dtype)
+    for g in range(4):
+        m = src[16 * g:16 * g + 16]
+        for i in range(16):
+            for r in range(4):
+                out[16 * g + i, r] = m[4 * r + i // 4, i % 4]
+    return out
+
+
+def tr_b8(lds, addrs):
+    """ds_read_b64_tr_b8 on byte ids; returns [64][8] byte ids."""
+    src = np.array([lds[a:a + 8] for a in addrs])
+    out = np.empty((64, 8), dtype=lds.dtype)
+    for g in range(4):
+        m = src[16 * g:16 * g + 16]
+        for i in range(16):
+            for r in range(8):
+                out[16 * g + i, r] = m[2 * r + i // 8, i % 8]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP16 forward kernel (BN = 64 keys per tile, 8 waves)
+# ---------------------------------------------------------------------------
+
+def fwd_consts(D):
+    CPR = D // 8
+    LPW = 64 * D * 2 // 1024 // 8
+    return CPR, LPW
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_k_tile(D):
+    """K: DMA fill, then the T-stage A operand (key block kb, k-step s): lane
+    (l32, hh) needs key key_of_row(32 kb + l32), d = 16 s + 8 hh .. +7; the
+    32x32 accumulator then holds key 16 (i / 8) + 8 hh + i % 8 in register i."""
+    CPR, LPW = fwd_consts(D)
+    k_swz = (lambda p: p & 15) if D == 128 else (lambda p: (p >> 1) & 7)
+    elem = -np.ones(64 * D, dtype=np.int64)  # LDS element -> key * D + d
+    for w in range(8):
+        for r in range(LPW):
+            for lane in range(64):
+                x = 64 * (w * LPW + r) + lane
+                row, slot = x // CPR, x % CPR
+                gchunk = slot ^ k_swz(row)
+                for e in range(8):
+                    assert elem[8 * x + e] == -1
+                    elem[8 * x + e] = key_of_row(row) * D + 8 * gchunk + e
+    assert sorted(elem) == list(range(64 * D))  # bijection
+    for kb in range(2):
+        for s in range(D // 16):
+            addrs = []
+            for lane in range(64):
+                l32, hh = lane % 32, lane // 32
+                p = 32 * kb + l32
+                off = (p * CPR + ((2 * s + hh) ^ k_swz(p))) * 16
+                got = elem[off // 2:off // 2 + 8]
+                want = key_of_row(p) * D + 16 * s + 8 * hh + np.arange(8)
+                assert np.array_equal(got, want)
+                addrs.append(off)
+            assert conflict_free(addrs, 16), (kb, s)
+    # accumulator register i of lane half hh holds MFMA row 8 (i / 4) + 4 hh + i % 4
+    for hh in range(2):
+        for i in range(16):
+            row = 8 * (i // 4) + 4 * hh + i % 4
+            assert key_of_row(row) == 16 * (i // 8) + 8 * hh + i % 8
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_v_staging_and_transpose(D):
+    """V: DMA into the natural-layout staging tile, ds_read_b64_tr_b16 pairs
+    that give lane l keys 8w .. 8w + 7 of d row 64h + l, then 16-byte V^T
+    stores into 144-byte rows, then the U-stage A operand reads."""
+    CPR, LPW = fwd_consts(D)
+    swz = lambda row: ((4 if D == 128 else 2) * (row & 3)) % CPR
+    elem = -np.ones(64 * D, dtype=np.int64)
+    for w in range(8):
+        for r in range(LPW):
+            for lane in range(64):
+                x = 64 * (w * LPW + r) + lane
+                row, pos = x // CPR, x % CPR
+                for e in range(8):
+                    assert elem[8 * x + e] == -1
+                    elem[8 * x + e] = row * D + 8 * (pos ^ swz(row)) + e
+    assert sorted(elem) == list(range(64 * D))
+    VT_STRIDE = 64 * 2 + 16
+    vt = -np.ones(D * VT_STRIDE // 2, dtype=np.int64)
+    for w in range(8):
+        for h in range(D // 64):
+            halves = []
+            for q in range(2):
+                addrs = []
+                for lane in range(64):
+                    i, gq = lane & 15, lane >> 4
+                    key = 8 * w + 4 * q + (i >> 2)
+                    c = 8 * h + 2 * gq + ((i & 3) >> 1)
+                    addrs.append(key * D * 2 + (c ^ swz(key)) * 16 + 8 * (i & 1))
+                assert conflict_free(addrs, 8), (w, h, q)
+                halves.append(tr_b16(elem, addrs))
+            waddrs = []
+            for lane in range(64):
+                keys = np.concatenate([halves[0][lane], halves[1][lane]])
+                want = (8 * w + np.arange(8)) * D + 64 * h + lane
+                assert np.array_equal(keys, want), (w, h, lane)
+                a = lane * VT_STRIDE + 8 * w * 2 + 64 * h * VT_STRIDE
+                vt[a // 2:a // 2 + 8] = keys
+                waddrs.append(a)
+            assert conflict_free(waddrs, 16)
+    # U-stage A operand: d row 32 b + l32, keys 16 s + 8 hh .. +7
+    for b in range(D // 32):
+        for s in range(4):
+            addrs = []
+            for lane in range(64):
+                l32, hh = lane % 32, lane // 32
+                a = l32 * VT_STRIDE + 16 * hh + 32 * b * VT_STRIDE + 32 * s
+                want = (16 * s + 8 * hh + np.arange(8)) * D + 32 * b + l32
+                assert np.array_equal(vt[a // 2:a // 2 + 8], want)
+                addrs.append(a)
+            assert conflict_free(addrs, 16)
+
+
+# ---------------------------------------------------------------------------
+# backward kernels: [row][d] tiles with chunk c of row r at c ^ swz(r)
+# ---------------------------------------------------------------------------
+
+def bwd_swz(D, r):
+    if D == 128:
+        return ((r & 3) << 2) | ((r >> 2) & 3)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+
+
+def bwd_off(D, row, col):
+    return row * D * 2 + 16 * ((col >> 3) ^ bwd_swz(D, row)) + 2 * (col & 7)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_tile_reads(D):
+    """Row operands (16 consecutive rows at one chunk) and the transposed
+    operands (pairs of ds_read_b64_tr_b16 giving lane l the d column
+    32 b + key_of_row(l % 32) of rows 8 hh .. 8 hh + 7 of a k-step) both
+    return the right elements without conflicts."""
+    rows = 64
+    lds = -np.ones(rows * D, dtype=np.int64)
+    for r in range(rows):
+        for c in range(D):
+            a = bwd_off(D, r, c)
+            assert lds[a // 2] == -1
+            lds[a // 2] = r * D + c
+    assert sorted(lds) == list(range(rows * D))
+    for s in range(D // 16):
+        for blk in range(2):
+            addrs = []
+            for lane in range(64):
+                l32, hh = lane % 32, lane // 32
+                row = key_of_row(l32) + 32 * blk
+                a = bwd_off(D, row, 16 * s + 8 * hh)
+                assert np.array_equal(lds[a // 2:a // 2 + 8], row * D + 16 * s + 8 * hh + np.arange(8))
+                addrs.append(a)
+            assert conflict_free(addrs, 16)
+    for b in range(D // 32):
+        for ks in range(rows // 16):
+            parts = []
+            for rd in range(2):
+                addrs = []
+                for lane in range(64):
+                    s16, g, hh = lane & 15, lane >> 4, lane >> 5
+                    sig = ((s16 & 1) << 1) | ((s16 >> 1) & 1)
+                    a = bwd_off(D, 8 * hh + 4 * rd + (s16 >> 2), 32 * b + 16 * (g & 1) + 4 * sig)
+                    addrs.append(a + ks * 16 * D * 2)
+                assert conflict_free(addrs, 8), (b, ks, rd)
+                parts.append(tr_b16(lds, addrs))
+            for lane in range(64):
+                hh = lane // 32
+                got = np.concatenate([parts[0][lane], parts[1][lane]])
+                col = 32 * b + key_of_row(lane % 32)
+                want = (16 * ks + 8 * hh + np.arange(8)) * D + col
+                assert np.array_equal(got, want), (b, ks, lane)
+
+
+# ---------------------------------------------------------------------------
+# FP8 forward kernel (E4M3 bytes, D = 128, 64-key tiles, 8 waves)
+# ---------------------------------------------------------------------------
+
+def test_fp8_k_and_v_tiles():
+    D = 128
+    k_swz = lambda r: (r >> 1) & 7
+    v_swz = lambda r: 2 * ((r >> 1) & 3)
+    kt = -np.ones(64 * D, dtype=np.int64)
+    vt = -np.ones(64 * D, dtype=np.int64)
+    for w in range(8):
+        for lane in range(64):
+            x = 64 * w + lane
+            r, pos = x >> 3, x & 7
+            krow = (r & ~31) | key_of_row(r & 31)
+            for e in range(16):
+                kt[16 * x + e] = krow * D + 16 * (pos ^ k_swz(r)) + e
+                vt[16 * x + e] = r * D + 16 * (pos ^ v_swz(r)) + e
+    assert sorted(kt) == list(range(64 * D)) and sorted(vt) == list(range(64 * D))
+    # T-stage A operand: two 16-byte reads, bytes d = 64 s + 32 hh .. +31 of
+    # key key_of_row(l32) of block kb
+    for kb in range(2):
+        for s in range(2):
+            for e in range(2):
+                addrs = []
+                for lane in range(64):
+                    l32, hh = lane % 32, lane // 32
+                    a = l32 * D + 16 * ((4 * s + 2 * hh + e) ^ k_swz(l32)) + kb * 32 * D
+                    key = 32 * kb + key_of_row(l32)
+                    want = key * D + 64 * s + 32 * hh + 16 * e + np.arange(16)
+                    assert np.array_equal(kt[a:a + 16], want)
+                    addrs.append(a)
+                assert conflict_free(addrs, 16)
+    # U-stage A operand: runs of 8 keys (16 rho + 8 hh .. +7) of d row
+    # 32 b + l32, by ds_read_b64_tr_b8 on the natural-layout V tile
+    for b in range(D // 32):
+        for rho in range(4):
+            addrs = []
+            for lane in range(64):
+                s16, g, hh = lane & 15, lane >> 4, lane >> 5
+                key = 8 * hh + (s16 >> 1)
+                addrs.append(key * D + 16 * ((2 * b + (g & 1)) ^ v_swz(key)) + 8 * (s16 & 1)
+                             + rho * 16 * D)
+            assert conflict_free(addrs, 8), (b, rho)
+            got = tr_b8(vt, addrs)
+            for lane in range(64):
+                hh = lane // 32
+                want = (16 * rho + 8 * hh + np.arange(8)) * D + 32 * b + lane % 32
+                assert np.array_equal(got[lane], want), (b, rho, lane)
+
+
+def test_conflict_model_detects_conflicts():
+    """Control: a plain row-major read of one column by 16 lanes conflicts."""
+    assert not conflict_free([256 * l for l in range(64)], 16)
+    assert conflict_free([16 * l for l in range(64)], 16)
+    assert not conflict_free([64 * l for l in range(64)], 8)

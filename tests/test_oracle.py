@@ -53,16 +53,18 @@ def test_half_decode_exhaustive_matches_numpy():
 
 # --- library special cases ---------------------------------------------------
 
+@pytest.mark.parametrize("scale", [0.37, -0.37, 0.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_identity_values_expose_softmax_matrix(causal):
+def test_identity_values_expose_softmax_matrix(causal, scale):
     """With V = I (N <= d) each output row is the softmax row itself. It is
     compared with scipy's softmax and logsumexp of scale * Q K^T. Q != K, so
-    a transposed product fails."""
+    a transposed product fails. Any finite scale is allowed: a negative one
+    favours the smallest q.k, zero gives uniform weights."""
     N, d = 12, 16
     q, k, _ = rand_qkv(1, 1, N, d, 7)
     v = np.zeros((1, 1, N, d), dtype=np.float16)
     v[0, 0, :, :N] = np.eye(N, dtype=np.float16)
-    scale = np.float32(0.37)
+    scale = np.float32(scale)
     o, lse = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
     s = float(scale) * (f64(q[0, 0]) @ f64(k[0, 0]).T)
     if causal:
@@ -122,9 +124,10 @@ def brute_row(q, k, v, i, causal, scale):
 
 @pytest.mark.parametrize("N,d", [(1, 1), (3, 2), (7, 5), (16, 8)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_brute_force_tiny(N, d, causal):
+@pytest.mark.parametrize("scale", [0.5, -0.5])
+def test_brute_force_tiny(N, d, causal, scale):
     q, k, v = rand_qkv(1, 1, N, d, 100 + N * d, lo=-1.5, hi=1.5)
-    scale = np.float32(0.5)
+    scale = np.float32(scale)
     o, lse = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
     for i in range(N):
         ro, rl = brute_row(q[0, 0], k[0, 0], v[0, 0], i, causal, float(scale))
@@ -148,6 +151,35 @@ def test_uniform_keys_give_mean_of_values(causal):
                                        rtol=0, atol=1e-14)
             s = float(scale) * float(f64(q[0, h, i]) @ f64(k[0, h, 0]))
             assert abs(lse[0, h, i] - (s + math.log(n))) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_mean_of_visible_values(causal):
+    """scale = 0: every visible score is 0, so O_i is the mean of the visible
+    value rows and lse_i = ln |J_i| whatever Q and K hold."""
+    B, H, N, d = 2, 2, 37, 8
+    q, k, v = rand_qkv(B, H, N, d, 23, lo=-50, hi=50)
+    o, lse = oracle.fmha_all(q, k, v, causal=causal, scale=np.float32(0.0))
+    if causal:
+        cnt = np.arange(1, N + 1, dtype=np.float64)
+        mean = np.cumsum(f64(v), axis=2) / cnt[None, None, :, None]
+        lse_ref = np.broadcast_to(np.log(cnt), (B, H, N))
+    else:
+        mean = np.broadcast_to(f64(v).mean(axis=2, keepdims=True), v.shape)
+        lse_ref = np.full((B, H, N), math.log(N))
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-14)
+
+
+def test_negative_scale_is_positive_scale_on_negated_queries():
+    """(-q).k * |scale| = q.k * scale term by term, and binary16 negation is
+    exact, so the two calls see the same scores bit for bit."""
+    q, k, v = rand_qkv(2, 2, 50, 16, 29)
+    a = oracle.fmha_all(q, k, v, causal=True, scale=np.float32(-0.3))
+    b = oracle.fmha_all(-q, k, v, causal=True, scale=np.float32(0.3))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = oracle.fmha_all(q, k, v, causal=True, scale=np.float32(0.3))
+    assert not np.allclose(a[0], c[0])
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -41,14 +41,16 @@ def all_rows(B, H, N):
 
 # --- library routine ---------------------------------------------------------
 
+@pytest.mark.parametrize("scale", [0.41, -0.41, 0.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_matches_torch_autograd(causal):
+def test_matches_torch_autograd(causal, scale):
     """Gradients of sum(dO * softmax(scale Q K^T) V) by torch.autograd in
-    float64, over 2 batches and 3 heads (b/h indexing) and a ragged N."""
+    float64, over 2 batches and 3 heads (b/h indexing) and a ragged N, for a
+    positive, a negative and a zero scale."""
     torch = pytest.importorskip("torch")
     B, H, N, d = 2, 3, 23, 8
     q, k, v, do = rand4(B, H, N, d, 11 + causal)
-    scale = np.float32(0.41)
+    scale = np.float32(scale)
     dq, dk, dv = oracle.fmha_bwd_all(q, k, v, do, causal=causal, scale=scale)
     Q, K, V = (torch.tensor(f64(x), requires_grad=True) for x in (q, k, v))
     s = float(scale) * (Q @ K.transpose(-1, -2))

@@ -19,6 +19,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "fmha_oracle.c")
 
 MUTANTS = {
     "scale dropped": ("s[j] = jb->scale * dot;", "s[j] = dot;"),
+    "sign of scale dropped": ("s[j] = jb->scale * dot;", "s[j] = fabs(jb->scale) * dot;"),
     "exp sign flipped": ("exp(s[j] - m)", "exp(m - s[j])"),
     "max not subtracted in weights": ("exp(s[j] - m)", "exp(s[j])"),
     "strict causal edge": ("jb->causal ? i + 1 : N", "jb->causal ? (i > 0 ? i : 1) : N"),
@@ -75,8 +76,9 @@ def _fp8_pin_calls():
 def _bwd_pin_calls():
     from tests import test_oracle_bwd as bp
     return [
-        lambda: bp.test_matches_torch_autograd(False),
-        lambda: bp.test_matches_torch_autograd(True),
+        lambda: bp.test_matches_torch_autograd(False, 0.41),
+        lambda: bp.test_matches_torch_autograd(True, 0.41),
+        lambda: bp.test_matches_torch_autograd(True, -0.41),
         lambda: bp.test_key_gradients_sum_to_zero(True),
         lambda: bp.test_value_gradients_sum_to_output_gradients(True),
         lambda: bp.test_uniform_keys_give_zero_query_gradient(False),
@@ -88,12 +90,15 @@ def _bwd_pin_calls():
 def _pin_calls():
     calls = [
         pins.test_half_decode_exhaustive_matches_numpy,
-        lambda: pins.test_identity_values_expose_softmax_matrix(False),
-        lambda: pins.test_identity_values_expose_softmax_matrix(True),
+        lambda: pins.test_identity_values_expose_softmax_matrix(False, 0.37),
+        lambda: pins.test_identity_values_expose_softmax_matrix(True, 0.37),
+        lambda: pins.test_identity_values_expose_softmax_matrix(True, -0.37),
+        lambda: pins.test_zero_scale_gives_mean_of_visible_values(True),
         lambda: pins.test_multihead_rows_match_library_reference(False),
         lambda: pins.test_multihead_rows_match_library_reference(True),
         pins.test_large_scores_do_not_overflow,
-        lambda: pins.test_brute_force_tiny(7, 5, True),
+        lambda: pins.test_brute_force_tiny(7, 5, True, 0.5),
+        lambda: pins.test_brute_force_tiny(7, 5, False, -0.5),
         lambda: pins.test_uniform_keys_give_mean_of_values(True),
         lambda: pins.test_one_hot_scores_select_one_value_row(64),
         pins.test_causal_first_row_is_first_value_row,
