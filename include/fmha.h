@@ -15,8 +15,9 @@
  * head dim 128.
  *
  * The library computes it in one fused kernel. Each step of the path runs
- * in the library's own HIP kernels. It allocates no device memory and keeps
- * no per-call state.
+ * in the library's own HIP kernels. It allocates no device memory at run
+ * time and keeps no per-call state (fmha_bwd_noalloc's fixed workspace
+ * aside).
  */
 #ifndef FMHA_H
 #define FMHA_H
@@ -138,6 +139,32 @@ int fmha_query_tile(int d);
 
 /* fmha_key_tile - keys per pipeline stage of that kernel (0 if unsupported). */
 int fmha_key_tile(int d);
+
+/* ---- no-allocation backward ----------------------------------------------
+ * fmha_bwd_noalloc - fmha_bwd without the ws argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid allocation.
+ *
+ * It runs the kernels of fmha_bwd on the same arguments (minus ws), with the
+ * same results bit for bit, and makes no allocating call. Its workspace is a
+ * fixed device array of 2 * FMHA_BWD_NOALLOC_MAX_ROWS floats (16 MiB), which
+ * the library holds on every GPU it runs on until the process ends; the
+ * first call on a device looks up its address there.
+ *
+ * Every call on one GPU shares that array: calls that overlap in time on one
+ * GPU (on different streams, or from different threads onto unordered
+ * streams) race and give wrong gradients. Calls ordered on one stream are
+ * safe; each call rewrites every workspace value it reads.
+ *
+ * Errors as for fmha_bwd, plus FMHA_ERR_TOO_LARGE (nothing enqueued) when
+ * B*H*N exceeds FMHA_BWD_NOALLOC_MAX_ROWS, and FMHA_ERR_HIP when the array's
+ * address cannot be had on the current device.
+ */
+#define FMHA_ERR_TOO_LARGE 4 /* the problem exceeds a fixed internal buffer */
+#define FMHA_BWD_NOALLOC_MAX_ROWS (1 << 21) /* B*H*N limit, e.g. B4 H32 N16384 */
+int fmha_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                     int B, int H, int N, int d, int causal, float scale, void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfmha.so")
-SOURCES = [os.path.join(CSRC, "fmha_api.hip"), os.path.join(CSRC, "ws_gemm_api.hip")]
+SOURCES = [os.path.join(CSRC, "fmha_api.hip"), os.path.join(CSRC, "ws_gemm_api.hip"),
+           os.path.join(CSRC, "fmha_noalloc.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -292,6 +292,7 @@ extern "C" const char* fmha_status_str(int status) {
     case FMHA_ERR_INVALID_ARGUMENT: return "invalid argument";
     case FMHA_ERR_UNSUPPORTED: return "unsupported head dim, alignment, size or descale";
     case FMHA_ERR_HIP: return "HIP launch failed";
+    case FMHA_ERR_TOO_LARGE: return "problem larger than the no-allocation entry point's workspace";
     default: return "unknown status";
   }
 }

@@ -17,9 +17,11 @@ FMHA_OK = 0
 FMHA_ERR_INVALID_ARGUMENT = 1
 FMHA_ERR_UNSUPPORTED = 2
 FMHA_ERR_HIP = 3
+FMHA_ERR_TOO_LARGE = 4
+FMHA_BWD_NOALLOC_MAX_ROWS = 1 << 21
 
 EXPORTS = ("fmha_fwd", "fmha_fwd_fp8", "fmha_bwd", "fmha_bwd_workspace_bytes",
-           "fmha_status_str", "fmha_query_tile", "fmha_key_tile")
+           "fmha_status_str", "fmha_query_tile", "fmha_key_tile", "fmha_bwd_noalloc")
 
 
 class FmhaError(RuntimeError):
@@ -54,6 +56,9 @@ def lib():
         l.fmha_bwd.restype = ctypes.c_int
         l.fmha_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float,
                                                                              ctypes.c_void_p]
+        l.fmha_bwd_noalloc.restype = ctypes.c_int
+        l.fmha_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [
+            ctypes.c_float, ctypes.c_void_p]
         l.fmha_bwd_workspace_bytes.restype = ctypes.c_size_t
         l.fmha_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
         l.fmha_status_str.restype = ctypes.c_char_p
@@ -86,6 +91,13 @@ def fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, causal, scale, s
     """The C entry point, pointers as integers. Returns the status code."""
     return lib().fmha_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, int(B), int(H), int(N), int(d),
                           int(causal), float(scale), stream)
+
+
+def fmha_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale,
+                     stream) -> int:
+    """The C entry point, pointers as integers. Returns the status code."""
+    return lib().fmha_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, int(B), int(H), int(N),
+                                  int(d), int(causal), float(scale), stream)
 
 
 def fmha_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
@@ -222,3 +234,38 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None
         raise FmhaError(st)
     return dq, dk, dv
 
+
+def backward_noalloc(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None,
+                     dq=None, dk=None, dv=None, stream=None):
+    """backward() through fmha_bwd_noalloc: the library's fixed workspace
+    instead of a caller buffer (B*H*N <= FMHA_BWD_NOALLOC_MAX_ROWS). Calls
+    that overlap in time on one GPU race on that workspace. Output tensors
+    are allocated here unless given."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.float16 or t.dim() != 4 or t.shape != q.shape:
+            raise ValueError("%s must be fp16 shaped like q" % name)
+        if not t.is_contiguous() or not t.is_cuda or t.device != q.device:
+            raise ValueError("%s must be contiguous and on q's GPU" % name)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != torch.float16 or not t.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous fp16 tensors shaped like q")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = fmha_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, H, N, d, causal, scale, handle)
+    if st != FMHA_OK:
+        raise FmhaError(st)
+    return dq, dk, dv

@@ -109,7 +109,7 @@ def test_empty_problem_is_ok_and_launches_nothing(field):
 
 
 def test_status_strings():
-    for s in range(4):
+    for s in range(5):
         assert fmha.fmha_status_str(s) and fmha.fmha_status_str(s) != "unknown status"
     assert fmha.fmha_status_str(99) == "unknown status"
 
@@ -180,20 +180,48 @@ def call_bwd(B=1, H=1, N=128, d=128, causal=0, scale=0.088, **ptrs):
                          p["dv"], p["ws"], B, H, N, d, causal, scale, None)
 
 
+def call_noalloc(B=1, H=1, N=128, d=128, causal=0, scale=0.088, **ptrs):
+    p = dict(BWD, **ptrs)
+    return fmha.fmha_bwd_noalloc(p["q"], p["k"], p["v"], p["o"], p["dout"], p["lse"], p["dq"],
+                                 p["dk"], p["dv"], B, H, N, d, causal, scale, None)
+
+
 @pytest.mark.parametrize("which", sorted(BWD))
 def test_bwd_null_pointer_is_invalid(which):
     assert call_bwd(**{which: 0}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+    if which != "ws":
+        assert call_noalloc(**{which: 0}) == fmha.FMHA_ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.parametrize("which", ["dq", "dk", "dv", "ws"])
 def test_bwd_output_aliasing_input_is_invalid(which):
     assert call_bwd(**{which: A}) == fmha.FMHA_ERR_INVALID_ARGUMENT
+    if which != "ws":
+        assert call_noalloc(**{which: 2 * A}) == fmha.FMHA_ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.parametrize("scale", [math.nan, math.inf])
 def test_bwd_non_finite_scale_is_invalid(scale):
     assert call_bwd(scale=scale) == fmha.FMHA_ERR_INVALID_ARGUMENT
+    assert call_noalloc(scale=scale) == fmha.FMHA_ERR_INVALID_ARGUMENT
 
 
 def test_bwd_empty_problem_is_ok():
-    assert call_bwd(N=0) == fmha.FMHA_OK
+    assert call_bwd(N=0) == fmha.FMHA_OK and call_noalloc(B=0) == fmha.FMHA_OK
+
+
+def test_noalloc_rejects_problems_beyond_its_workspace():
+    # B*H*N one row past the fixed workspace: refused before any HIP call
+    big = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, dout=5 << 40, lse=6 << 40, dq=7 << 40,
+               dk=8 << 40, dv=9 << 40)
+    rows = fmha.FMHA_BWD_NOALLOC_MAX_ROWS
+    assert call_noalloc(B=1, H=1, N=rows + 1, d=64, **big) == fmha.FMHA_ERR_TOO_LARGE
+    assert call_noalloc(B=4, H=32, N=16385, d=128, **big) == fmha.FMHA_ERR_TOO_LARGE
+    assert "workspace" in fmha.fmha_status_str(fmha.FMHA_ERR_TOO_LARGE)
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FMHA_BWD_NOALLOC_MAX_ROWS \(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == fmha.FMHA_BWD_NOALLOC_MAX_ROWS
+    assert re.search(r"#define FMHA_ERR_TOO_LARGE %d\b" % fmha.FMHA_ERR_TOO_LARGE, text)
