@@ -1,8 +1,9 @@
 // Fused multi-head attention forward pass for gfx950 (MI355X, CDNA4).
 //
 // The kernel is persistent: one workgroup per CU walks the (batch, head,
-// query tile) tiles, one at a time. Per tile the query rows stay in VGPRs. Key/value tiles stream from HBM into LDS rings
-// by LDS-DMA. Each stage of the pages maps onto gfx950 units:
+// query tile) tiles, one at a time. Per tile the query rows stay in VGPRs.
+// Key/value tiles stream from HBM into LDS rings by LDS-DMA. Each stage of
+// the pages maps onto gfx950 units:
 // - T stage, S = Q K^T (Tawa, section III-D): fp16 MFMA, fp32 accumulate;
 // - C stage, online softmax with rescale (PipeThreader's softmax and
 //   rescale tasks): VALU, exp2 on the transcendental unit;
@@ -18,10 +19,9 @@
 //   i of lane-half h holds key 16*(i/8) + 8*h + i%8. Eight consecutive
 //   registers therefore cover 8 consecutive keys. After conversion to fp16
 //   they are the B operand of O^T += V^T P^T, with no shuffle.
-// * V is stored transposed in LDS ([d][key], keys contiguous). One 16-byte
-//   LDS read then yields the matching A operand (8 keys of one d column).
-//   The transpose happens LDS to LDS: V arrives in natural layout and
-//   ds_read_b64_tr_b16 returns it column-wise.
+// * V stays in natural [key][d] layout in LDS. The A operand of the U stage
+//   (eight consecutive keys of one d column per lane) comes from two
+//   ds_read_b64_tr_b16, each returning four keys of one column per lane.
 // * O^T accumulates with one query per lane column. The per-row rescale
 //   factor is therefore a per-lane scalar.
 // * Row sums of P run on the matrix core as well (one 16x16x32 MFMA per PV
@@ -85,16 +85,9 @@ struct Tile {
   static constexpr int DBLK = D / 32;           // 32-row blocks of O^T
   static constexpr int PSTEPS = BN / 16;        // MFMA k-steps of PV
   static constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
-  static constexpr int TILE_BYTES = BN * D * 2; // one K tile in LDS
-  static constexpr int VT_STRIDE = BN * 2 + 16; // bytes per d row of a V^T tile (16-byte pad)
-  static constexpr int VT_BYTES = D * VT_STRIDE;  // one V^T tile in LDS
-  static constexpr int SLOTS = 3;               // ring depth for K and for V^T
-  static constexpr int STAGE_SLOTS = 3;         // ring depth for V tiles in natural layout
-  static constexpr int LDS_BYTES = SLOTS * (TILE_BYTES + VT_BYTES) + STAGE_SLOTS * TILE_BYTES;
-  // V^T production: wave w writes keys 8w .. 8w+7 of d rows lane + 64*h
-  static constexpr int V_KEYS_PER_WAVE = BN / WAVES;
-  static constexpr int V_COLS = D / 64;          // d rows per lane (1 or 2)
-  static_assert(V_KEYS_PER_WAVE == 8 && V_COLS * 64 == D, "V^T production covers the tile");
+  static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
+  static constexpr int SLOTS = 4;               // ring depth for K and for V
+  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
   // one tile = TILE_BYTES / 1024 wave-wide 16-byte-per-lane LDS-DMA loads
   static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;  // per tile
@@ -167,10 +160,8 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw) {
   using T = Tile<D>;
   typedef __attribute__((address_space(3))) char lds_char;
-  typedef __attribute__((address_space(3))) half8 lds_half8;
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
-  lds_char* const v_stage = v_ring + T::SLOTS * T::VT_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,10 +231,11 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   const int n_wave = CAUSAL ? min(n_kv, (wave_q_lo + T::QW - 1) / T::BN + 1) : n_kv;
 
   // ---- producers ---------------------------------------------------------------
-  // K: HBM -> LDS ring slot by LDS-DMA, no register staging. Wave w issues
-  // loads w*LOADS_PER_WAVE .. +LOADS_PER_WAVE-1 of a tile; load i fills the
-  // tile's LDS chunks 64*i .. 64*i+63 (one per lane), and each lane fetches
-  // the global chunk that the swizzled layout puts there.
+  // K and V: HBM -> LDS ring slots by LDS-DMA, no register staging. Wave w
+  // issues loads w*LOADS_PER_WAVE .. +LOADS_PER_WAVE-1 of a tile; load i
+  // fills the tile's LDS chunks 64*i .. 64*i+63 (one per lane), and each lane
+  // fetches the global chunk that the swizzled layout puts there. Both rings
+  // have SLOTS slots (slot = tile % SLOTS).
   int k_src[T::LOADS_PER_WAVE];
 #pragma unroll
   for (int r = 0; r < T::LOADS_PER_WAVE; ++r) {
@@ -251,15 +243,15 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     const int row = x / T::CPR, slot = x % T::CPR;
     k_src[r] = (key_of_row(row) * D + 8 * (slot ^ k_swz<D>(row))) * 2;
   }
-  auto fetch_k = [&](int j, int slot) __attribute__((always_inline)) {
-    lds_char* dst = k_ring + slot * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
+  auto fetch_k = [&](int j) __attribute__((always_inline)) {
+    lds_char* dst = k_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
 #pragma unroll
     for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
       load16_to_lds(rk, j * T::BN * D * 2 + k_src[i], dst + i * 1024);
   };
-  // V: HBM -> a 3-slot staging ring in natural [key][d] layout by LDS-DMA,
-  // three tiles ahead. Chunk c of key row k is stored at chunk c ^ v_swz(k),
-  // so that the transposing reads below touch distinct banks.
+  // V stays in natural [key][d] layout; chunk c of key row k is stored at
+  // chunk c ^ v_swz(k), so that the transposing operand reads below touch
+  // distinct banks.
   auto v_swz = [](int row) __attribute__((always_inline)) {
     return ((D == 128 ? 4 : 2) * (row & 3)) % T::CPR;
   };
@@ -271,65 +263,44 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     v_src[r] = (row * D + 8 * (pos ^ v_swz(row))) * 2;
   }
   auto fetch_v = [&](int j) __attribute__((always_inline)) {
-    lds_char* dst = v_stage + (j % T::STAGE_SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
+    lds_char* dst = v_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * T::LOADS_PER_WAVE * 1024;
 #pragma unroll
     for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
       load16_to_lds(rv, j * T::BN * D * 2 + v_src[i], dst + i * 1024);
   };
-  // Staging -> V^T ([d][key], rows padded to VT_STRIDE bytes) with
-  // ds_read_b64_tr_b16. In each 16-lane group g, source lane i reads 4
-  // d-values (d0 + 4*(i%4) ..) of key k0 + i/4, and result lane i receives
-  // d0 + i of keys k0 .. k0+3. With d0 = 64h + 16g and k0 = 8w + 4q, lane l
-  // ends with keys 8w .. 8w+7 of d row 64h + l: one 16-byte V^T store.
-  int tr_src[T::V_COLS][2];
-#pragma unroll
-  for (int h = 0; h < T::V_COLS; ++h)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = lane & 15, gq = lane >> 4;
-      const int key = T::V_KEYS_PER_WAVE * wave + 4 * q + (i >> 2);
-      const int c = 8 * h + 2 * gq + ((i & 3) >> 1);
-      tr_src[h][q] = key * D * 2 + ((c ^ v_swz(key)) * 16) + 8 * (i & 1);
-    }
-  shortx4 vtr[T::V_COLS][2];
-  auto tr_read = [&](int j) __attribute__((always_inline)) {
-    const lds_char* st = v_stage + (j % T::STAGE_SLOTS) * T::TILE_BYTES;
-#pragma unroll
-    for (int h = 0; h < T::V_COLS; ++h)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        // Inline asm: the compiler would otherwise wait for every LDS-DMA in
-        // flight (vmcnt(0)) before this read, though none targets this slot.
-        // The matching lgkmcnt wait is explicit in tr_write.
-        asm volatile("ds_read_b64_tr_b16 %0, %1"
-                     : "=v"(vtr[h][q])
-                     : "v"((uint32_t)(uintptr_t)(st + tr_src[h][q])));
-  };
-  auto tr_write = [&](int j) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_char* vt = v_ring + (j % T::SLOTS) * T::VT_BYTES + lane * T::VT_STRIDE +
-                   T::V_KEYS_PER_WAVE * wave * 2;
-#pragma unroll
-    for (int h = 0; h < T::V_COLS; ++h) {
-      intx4 w;
-      w[0] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][0], vtr[h][0], 0, 1));
-      w[1] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][0], vtr[h][0], 2, 3));
-      w[2] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][1], vtr[h][1], 0, 1));
-      w[3] = __builtin_bit_cast(int, __builtin_shufflevector(vtr[h][1], vtr[h][1], 2, 3));
-      *(__attribute__((address_space(3))) intx4*)(vt + 64 * h * T::VT_STRIDE) = w;
-    }
-  };
 
-  // ---- consumer-side LDS offsets (per lane, constant over the loop) ----------
+  // ---- consumer-side LDS addresses (per lane, constant over the loop) --------
+  // The operand reads are inline asm with explicit lgkmcnt waits: as
+  // builtins, the compiler would wait for every LDS-DMA in flight (vmcnt(0))
+  // before them, though none targets the slots read. Each address is a lane
+  // register plus an immediate (slot, key block, k-step).
   // QK^T A operand: row 32*kb + l32 of the K tile, chunk 2*s + hh. The
   // swizzle depends on the row only through its low 4 bits, so the 32-row
   // block kb adds a constant.
-  int k_rd[T::KSTEPS];
+  uint32_t k_rd[T::KSTEPS];
 #pragma unroll
-  for (int s = 0; s < T::KSTEPS; ++s) k_rd[s] = k_chunk_off<D>(l32, 2 * s + hh);
+  for (int s = 0; s < T::KSTEPS; ++s)
+    k_rd[s] = (uint32_t)(uintptr_t)k_ring + k_chunk_off<D>(l32, 2 * s + hh);
   constexpr int K_BLOCK_BYTES = 32 * T::CPR * 16;
-  // PV A operand: V^T row 32*b + l32, keys 16*s + 8*hh .. +7 (16 bytes).
-  const int vt_rd = l32 * T::VT_STRIDE + 16 * hh;
+  // PV A operand (d block b, k-step st): lane l needs d = 32b + l % 32 of
+  // keys 16st + 8hh .. +7, eight keys of one V column: two ds_read_b64_tr_b16
+  // of four keys each. In 16-lane group g, source lane s reads the four d
+  // values 32b + 16(g % 2) + 4(s % 4) .. +3 of key 16st + 8hh + 4r + s / 4
+  // (read r = 0, 1); result lane i of the group then holds d
+  // 32b + 16(g % 2) + i of those four keys. The key's low two bits are s / 4
+  // whatever st and r are, so the swizzle is fixed per lane and d block.
+  uint32_t v_rd[T::DBLK];
+  {
+    const int s16 = lane & 15, g = lane >> 4;
+    const int key = 8 * hh + (s16 >> 2);
+#pragma unroll
+    for (int b = 0; b < T::DBLK; ++b) {
+      const int c = 4 * b + 2 * (g & 1) + ((s16 & 3) >> 1);
+      v_rd[b] = (uint32_t)(uintptr_t)v_ring + key * D * 2 + 16 * (c ^ v_swz(key)) + 8 * (s16 & 1);
+    }
+  }
+  constexpr int V_R_BYTES = 4 * D * 2;    // read r = 1: four keys on
+  constexpr int V_ST_BYTES = 16 * D * 2;  // next k-step: sixteen keys on
 
   floatx16 sacc[T::KB];   // S_j^T (fp32)
   half8 pf[T::PSTEPS];    // P_j^T in fp16: B operand of PV_j
@@ -338,31 +309,54 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones_a, pf[st], lacc, 0, 0, 0);
   };
 
-  // T stage for key tile j: S^T = K_j Q^T.
-  auto qk = [&](auto slot) __attribute__((always_inline)) {
-    const lds_char* ks = k_ring + slot * T::TILE_BYTES;
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-    for (int s = 0; s < T::KSTEPS; ++s)
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        const half8 a = *(const lds_half8*)(ks + k_rd[s] + kb * K_BLOCK_BYTES);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[s], sacc[kb], 0, 0, 0);
-      }
+  // Operand reads (issue only; the caller waits). A T operand is one
+  // ds_read_b128, a U operand two ds_read_b64_tr_b16.
+  auto read_t = [&](auto slot_tag, int n) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    const int kb = n % T::KB, st = n / T::KB;
+    half8 a;
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(a)
+                 : "v"(k_rd[st]), "i"(SLOT * T::TILE_BYTES + kb * K_BLOCK_BYTES));
+    return a;
   };
-  // U stage for key tile j: O^T += V_j^T P_j^T.
-  auto pv = [&](auto slot) __attribute__((always_inline)) {
-    const lds_char* vs = v_ring + slot * T::VT_BYTES + vt_rd;
+  auto read_u = [&](auto slot_tag, int n) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    const int st = n / T::DBLK, b = n % T::DBLK;
+    shortx4 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(lo)
+                 : "v"(v_rd[b]), "i"(SLOT * T::TILE_BYTES + st * V_ST_BYTES));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi)
+                 : "v"(v_rd[b]), "i"(SLOT * T::TILE_BYTES + st * V_ST_BYTES + V_R_BYTES));
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // T stage of key tile 0 alone: S^T = K_0 Q^T.
+  auto qk = [&]() __attribute__((always_inline)) {
+    using S0 = std::integral_constant<int, 0>;
 #pragma unroll
-    for (int s = 0; s < T::PSTEPS; ++s)
+    for (int st = 0; st < T::KSTEPS; ++st) {
+      half8 a[T::KB];
 #pragma unroll
-      for (int b = 0; b < T::DBLK; ++b) {
-        const half8 a = *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * s);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[b], 0, 0, 0);
-      }
+      for (int kb = 0; kb < T::KB; ++kb) a[kb] = read_t(S0{}, st * T::KB + kb);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[T::KB - 1]));
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[kb], qf[st], st == 0 ? floatx16{} : sacc[kb],
+                                                          0, 0, 0);
+    }
+  };
+  // U stage of a wave's last key tile alone: O^T += V^T P^T, V in `slot`.
+  auto pv = [&](auto slot_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < T::PSTEPS * T::DBLK; ++n) {
+      half8 a = read_u(slot_tag, n);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a));
+      const int st = n / T::DBLK, b = n % T::DBLK;
+      oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[st], oacc[b], 0, 0, 0);
+    }
 #pragma unroll
     for (int s = 0; s < T::PSTEPS; ++s) row_sum(s);
   };
@@ -440,19 +434,19 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
       exp_pack();
     }
   };
-  // Matrix-core interval of a steady iteration: U_{j-1} (V^T slot PREV) and
-  // T_j (K slot U), 2 * NPV MFMAs in a fixed order, plus the row-sum MFMA
-  // after the last U MFMA of each k-step. Even slots are U MFMAs, odd slots
-  // T MFMAs, so consecutive MFMAs never share an accumulator. Each
-  // LDS operand is read OPERAND_AHEAD slots before its MFMA; scheduling
-  // barriers keep that order, so each MFMA waits only for its own operand.
-  // Slot order: the first LEAD_U slots are U MFMAs, whose V^T operands the
-  // wave already read at the end of its vector interval (V^T_{j-1} is
-  // complete one interval before U_{j-1}; K_j is complete only when this
-  // interval starts). Then T and U alternate, and the last LEAD_U slots are
-  // T MFMAs. T slot n is key block n % KB at k-step n / KB and U slot n is
-  // d block n % DBLK at k-step n / DBLK, so consecutive MFMAs of one kind
-  // never share an accumulator either.
+  // Matrix-core interval of a steady iteration: U_{j-1} (V slot (j-1) % 4)
+  // and T_j (K slot j % 4), 2 * NPV MFMAs in a fixed order, plus the row-sum
+  // MFMA after the last U MFMA of each k-step. Each operand is read
+  // OPERAND_AHEAD slots before its MFMA; scheduling barriers keep that order,
+  // and each MFMA waits (lgkmcnt) only for its own operand: LDS reads
+  // complete in order, so the later operands' reads may still be pending.
+  // Slot order: the first LEAD_U slots are U MFMAs, whose V operands the wave
+  // read at the end of its vector interval (V_{j-1} is visible two intervals
+  // before U_{j-1}; K_j only when this interval starts, so K operands cannot
+  // be read early). Then T and U alternate, and the last LEAD_U slots are T
+  // MFMAs. T slot n is key block n % KB at k-step n / KB and U slot n is d
+  // block n % DBLK at k-step n / DBLK, so consecutive MFMAs never share an
+  // accumulator.
   constexpr int NPV = T::PSTEPS * T::DBLK;
   constexpr int NM = 2 * NPV;
   static_assert(NPV == T::KSTEPS * T::KB, "as many U as T MFMAs");
@@ -465,38 +459,33 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   auto slot_n = [](int i) constexpr {
     return i < LEAD_U ? i : (i >= NM - LEAD_U ? i - NPV : (i - LEAD_U) / 2 + (((i - LEAD_U) & 1) ? LEAD_U : 0));
   };
-  auto u_operand = [&](const lds_char* vs, int n) __attribute__((always_inline)) {
-    const int st = n / T::DBLK, b = n % T::DBLK;
-    return *(const lds_half8*)(vs + 32 * b * T::VT_STRIDE + 32 * st);
+  // LDS reads of slots i+1 .. i+AHEAD: those may still be outstanding when
+  // slot i's operand has landed
+  auto reads_after = [slot_is_u](int i) constexpr {
+    int r = 0;
+    for (int m = i + 1; m <= i + AHEAD && m < NM; ++m) r += slot_is_u(m) ? 2 : 1;
+    return r;
   };
-  auto t_operand = [&](const lds_char* ks, int n) __attribute__((always_inline)) {
-    const int kb = n % T::KB, st = n / T::KB;
-    return *(const lds_half8*)(ks + k_rd[st] + kb * K_BLOCK_BYTES);
-  };
+  static_assert(2 * AHEAD <= 15, "the wait count fits lgkmcnt");
   half8 ring[AHEAD];
   // End of a vector interval: the lead U operands of the next matrix-core
-  // interval, U_{j-1} with V^T slot PREV of that interval.
-  auto prefetch_lead = [&](auto u_tag) __attribute__((always_inline)) {
-    constexpr int PREV = (decltype(u_tag)::value + 2) % 3;
-    const lds_char* vs = v_ring + PREV * T::VT_BYTES + vt_rd;
+  // interval (U_j, V slot j % 4).
+  auto prefetch_lead = [&](auto v_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LEAD_U; ++i) ring[i] = u_operand(vs, i);
+    for (int i = 0; i < LEAD_U; ++i) ring[i] = read_u(v_tag, i);
   };
-  auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
-    constexpr int U = decltype(u_tag)::value;
-    constexpr int PREV = (U + 2) % 3;
-    const lds_char* ks = k_ring + U * T::TILE_BYTES;
-    const lds_char* vs = v_ring + PREV * T::VT_BYTES + vt_rd;
+  auto mfma_interval = [&](auto k_tag, auto v_tag) __attribute__((always_inline)) {
     auto operand = [&](int i) __attribute__((always_inline)) {
-      return slot_is_u(i) ? u_operand(vs, slot_n(i)) : t_operand(ks, slot_n(i));
+      return slot_is_u(i) ? read_u(v_tag, slot_n(i)) : read_t(k_tag, slot_n(i));
     };
 #pragma unroll
     for (int i = LEAD_U; i < AHEAD; ++i) ring[i] = operand(i);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const half8 a = ring[i % AHEAD];
+      half8 a = ring[i % AHEAD];
       if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(reads_after(i)));
       const int n = slot_n(i);
       if (slot_is_u(i)) {
         const int st = n / T::DBLK, b = n % T::DBLK;
@@ -514,92 +503,90 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // ---- ping-pong schedule -------------------------------------------------------
   // Every wave runs the same sequence of barrier-separated local intervals.
   // 2j is the matrix-core interval of iteration j: U_{j-1} and T_j. 2j+1 is
-  // the vector interval: the producer work (transpose V_{j+1} into V^T, DMA
-  // K_{j+2} and V_{j+3}) and C_j (mask, exp2, fp16 pack, row max, and when
-  // needed the lazy rescale). Group 1 starts one interval late
-  // (an extra barrier up front, which group 0 matches at the end), so in every
-  // interval one wave of each SIMD feeds the matrix core while the other runs
-  // the vector work. Global interval = local interval + group.
+  // the vector interval: the DMAs of K_{j+2} and V_{j+2}, C_j (mask, exp2,
+  // fp16 pack, row max, and when needed the lazy rescale), then the lead V
+  // operands of U_j. Group 1 starts one interval late (an extra barrier up
+  // front, which group 0 matches at the end), so in every interval one wave
+  // of each SIMD feeds the matrix core while the other runs the vector work.
+  // Global interval = local interval + group.
   //
-  // Rings (slot = tile % 3).
-  // - K_t: DMA issued in local 2t-3, waited for at the end of local 2t-2
-  //   (mfma_sync), read in global 2t .. 2t+1; the next DMA into its slot is
-  //   issued in local 2t+3.
-  // - V_t (natural layout): DMA issued in local 2t-5, waited for at the end
-  //   of local 2t-3 (vector_sync), transposed in global 2t-1 .. 2t; the next
-  //   DMA into its slot is issued in local 2t+1.
-  // - V^T_t: written in global 2t-1 .. 2t, read in global 2t+2 .. 2t+3; the
-  //   next write to its slot is in global 2t+5.
-  // Each wait is followed by a barrier before any other wave reads. Loads
-  // past the sequence end return zeros into slots that are never read.
+  // Rings (slot = tile % 4). K_t and V_t are issued in local 2t-3 and waited
+  // for at the end of local 2t-2 (vmcnt(0): nothing is issued after them
+  // before local 2t-1); after the barrier ending global 2t-1 every wave's
+  // share has landed. K_t is read in global 2t .. 2t+1, V_t from global 2t+1
+  // (group 0's lead operands of U_t) to 2t+3. The next DMA into either slot
+  // (tile t+4) is issued in global 2t+5 or later. Loads past the sequence
+  // end return zeros into slots that are never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
-    // this wave's K_{j+1} DMA landed (V_{j+3}, issued after it, may not have)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
+    // this wave's K_{j+1} and V_{j+1} DMAs landed
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto vector_sync = [&]() __attribute__((always_inline)) {
-    // this wave's V^T writes are in LDS and its V_{j+2} DMA landed
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
-  };
-  auto produce_issue = [&](int j) __attribute__((always_inline)) {
-    tr_read(j + 1);
-    fetch_k(j + 2, (j + 2) % T::SLOTS);
-    fetch_v(j + 3);
+    // this wave's lead operand reads are done
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto produce = [&](int j) __attribute__((always_inline)) {
-    produce_issue(j);
-    tr_write(j + 1);
+    fetch_k(j + 2);
+    fetch_v(j + 2);
   };
 
-  // Steady-state iteration j (1 <= j < n_wave) with U = j % 3 known at
-  // compile time, so every LDS operand address is a lane register plus an
-  // immediate.
+  // Steady-state iteration j (1 <= j < n_wave) with K slot U = j % 4 known
+  // at compile time (V slot (U + 3) % 4), so every LDS operand address is a
+  // lane register plus an immediate.
   auto steady = [&](int j, auto u_tag, auto exact_tag) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_tag)::value;
     // local interval 2j: matrix core
     __builtin_amdgcn_s_setprio(1);
-    mfma_interval(u_tag);
+    mfma_interval(u_tag, std::integral_constant<int, (U + 3) % 4>{});
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     // local interval 2j+1: vector ALU
-    produce_issue(j);
+    produce(j);
     if constexpr (decltype(exact_tag)::value) softmax(j);
     else softmax_fast(j);
-    tr_write(j + 1);
-    prefetch_lead(std::integral_constant<int, (decltype(u_tag)::value + 1) % 3>{});
+    prefetch_lead(u_tag);
     vector_sync();
   };
   using U0 = std::integral_constant<int, 0>;
   using U1 = std::integral_constant<int, 1>;
   using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
+  static_assert(T::SLOTS == 4, "the unrolled loop walks four-slot rings");
+  // U stage of a wave's last key tile j - 1 (V slot (j - 1) % 4)
+  auto last_pv = [&](int j) __attribute__((always_inline)) {
+    switch ((j - 1) & 3) {
+      case 0: pv(U0{}); break;
+      case 1: pv(U1{}); break;
+      case 2: pv(U2{}); break;
+      default: pv(U3{}); break;
+    }
+  };
 
   // The whole K/V pipeline; the fast variant skips the row max after tile 0.
   auto run_pipeline = [&](auto exact_tag) __attribute__((always_inline)) {
-    fetch_k(0, 0);
+    fetch_k(0);
     fetch_v(0);
-    fetch_k(1, 1);
+    fetch_k(1);
     fetch_v(1);
-    fetch_v(2);
-    // K_0 and V_0 landed in every wave
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(3 * T::LOADS_PER_WAVE) : "memory");
-    tr_read(0);
-    tr_write(0);
-    // V^T_0 written; K_1 and V_1 landed in every wave (V_2 may be in flight)
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LOADS_PER_WAVE) : "memory");
+    // K_0 and V_0 landed in every wave (K_1 and V_1 may be in flight)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
     if (group == 1) sync();
 
     // j = 0: T_0, then C_0
-    if (n_wave > 0) qk(U0{});
+    if (n_wave > 0) qk();
     mfma_sync();
     produce(0);
     if (n_wave > 0) softmax(0);
-    prefetch_lead(U1{});
+    prefetch_lead(U0{});
     vector_sync();
     // 1 <= j < n_wave: U_{j-1}, T_j, then C_j
     int j = 1;
-    for (; j + 3 <= n_wave; j += 3) {
+    for (; j + 4 <= n_wave; j += 4) {
       steady(j, U1{}, exact_tag);
       steady(j + 1, U2{}, exact_tag);
-      steady(j + 2, U0{}, exact_tag);
+      steady(j + 2, U3{}, exact_tag);
+      steady(j + 3, U0{}, exact_tag);
     }
     if (j < n_wave) {
       steady(j, U1{}, exact_tag);
@@ -607,12 +594,16 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
       if (j < n_wave) {
         steady(j, U2{}, exact_tag);
         ++j;
+        if (j < n_wave) {
+          steady(j, U3{}, exact_tag);
+          ++j;
+        }
       }
     }
     // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
     // which the wave still produces its share of the workgroup's tiles
     for (; j <= n_kv; ++j) {
-      if (j == n_wave && j >= 1) pv((j - 1) % T::SLOTS);
+      if (j == n_wave && j >= 1) last_pv(j);
       mfma_sync();
       produce(j);
       vector_sync();
@@ -633,10 +624,10 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     // reruns with the row max and lazy rescale (the rings are idle here).
     const float l_fast = sum_halves(lacc[0]);
     const bool bad = __builtin_amdgcn_ballot_w64(!(l_fast < INFINITY)) != 0;
-    // the flags sit in the staging ring, which trailing DMAs of other waves
-    // may still be writing until every wave has passed its vmcnt(0)
+    // the flags sit in the V ring, which trailing DMAs of other waves may
+    // still be writing until every wave has passed its vmcnt(0)
     sync();
-    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)v_stage;
+    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)v_ring;
     if (lane == 0) flags[wave] = bad ? 1 : 0;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     int any = 0;

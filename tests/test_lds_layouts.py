@@ -118,10 +118,11 @@ def test_fwd_k_tile(D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_fwd_v_staging_and_transpose(D):
-    """V: DMA into the natural-layout staging tile, ds_read_b64_tr_b16 pairs
-    that give lane l keys 8w .. 8w + 7 of d row 64h + l, then 16-byte V^T
-    stores into 144-byte rows, then the U-stage A operand reads."""
+def test_fwd_v_tile_and_transposed_operand(D):
+    """V: DMA into a natural-layout tile, then the U-stage A operand read
+    straight from it: for d block b and k-step st, lane l needs d = 32 b +
+    l % 32 of keys 16 st + 8 hh .. +7, from two ds_read_b64_tr_b16 of four
+    keys each."""
     CPR, LPW = fwd_consts(D)
     swz = lambda row: ((4 if D == 128 else 2) * (row & 3)) % CPR
     elem = -np.ones(64 * D, dtype=np.int64)
@@ -134,40 +135,24 @@ def test_fwd_v_staging_and_transpose(D):
                     assert elem[8 * x + e] == -1
                     elem[8 * x + e] = row * D + 8 * (pos ^ swz(row)) + e
     assert sorted(elem) == list(range(64 * D))
-    VT_STRIDE = 64 * 2 + 16
-    vt = -np.ones(D * VT_STRIDE // 2, dtype=np.int64)
-    for w in range(8):
-        for h in range(D // 64):
+    for b in range(D // 32):
+        for st in range(4):
             halves = []
-            for q in range(2):
+            for r in range(2):
                 addrs = []
                 for lane in range(64):
-                    i, gq = lane & 15, lane >> 4
-                    key = 8 * w + 4 * q + (i >> 2)
-                    c = 8 * h + 2 * gq + ((i & 3) >> 1)
-                    addrs.append(key * D * 2 + (c ^ swz(key)) * 16 + 8 * (i & 1))
-                assert conflict_free(addrs, 8), (w, h, q)
+                    s16, g, hh = lane & 15, lane >> 4, lane >> 5
+                    key = 8 * hh + (s16 >> 2)
+                    c = 4 * b + 2 * (g & 1) + ((s16 & 3) >> 1)
+                    base = key * D * 2 + 16 * (c ^ swz(key)) + 8 * (s16 & 1)
+                    addrs.append(base + st * 16 * D * 2 + r * 4 * D * 2)
+                assert conflict_free(addrs, 8), (b, st, r)
                 halves.append(tr_b16(elem, addrs))
-            waddrs = []
             for lane in range(64):
-                keys = np.concatenate([halves[0][lane], halves[1][lane]])
-                want = (8 * w + np.arange(8)) * D + 64 * h + lane
-                assert np.array_equal(keys, want), (w, h, lane)
-                a = lane * VT_STRIDE + 8 * w * 2 + 64 * h * VT_STRIDE
-                vt[a // 2:a // 2 + 8] = keys
-                waddrs.append(a)
-            assert conflict_free(waddrs, 16)
-    # U-stage A operand: d row 32 b + l32, keys 16 s + 8 hh .. +7
-    for b in range(D // 32):
-        for s in range(4):
-            addrs = []
-            for lane in range(64):
-                l32, hh = lane % 32, lane // 32
-                a = l32 * VT_STRIDE + 16 * hh + 32 * b * VT_STRIDE + 32 * s
-                want = (16 * s + 8 * hh + np.arange(8)) * D + 32 * b + l32
-                assert np.array_equal(vt[a // 2:a // 2 + 8], want)
-                addrs.append(a)
-            assert conflict_free(addrs, 16)
+                hh = lane // 32
+                got = np.concatenate([halves[0][lane], halves[1][lane]])
+                want = (16 * st + 8 * hh + np.arange(8)) * D + 32 * b + lane % 32
+                assert np.array_equal(got, want), (b, st, lane)
 
 
 # ---------------------------------------------------------------------------
