@@ -56,8 +56,7 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 constexpr float RESCALE_LOG2 = 8.0f;
 // MFMA slots by which an LDS operand read precedes its MFMA.
 constexpr int OPERAND_AHEAD = 4;
-// U MFMAs at the head of a matrix-core interval whose operands are read in
-// the wave's preceding vector interval.
+// U MFMAs at the head of a matrix-core interval (T MFMAs close it).
 constexpr int LEAD_U = 2;
 
 struct Params {
@@ -440,11 +439,10 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // OPERAND_AHEAD slots before its MFMA; scheduling barriers keep that order,
   // and each MFMA waits (lgkmcnt) only for its own operand: LDS reads
   // complete in order, so the later operands' reads may still be pending.
-  // Slot order: the first LEAD_U slots are U MFMAs, whose V operands the wave
-  // read at the end of its vector interval (V_{j-1} is visible two intervals
-  // before U_{j-1}; K_j only when this interval starts, so K operands cannot
-  // be read early). Then T and U alternate, and the last LEAD_U slots are T
-  // MFMAs. T slot n is key block n % KB at k-step n / KB and U slot n is d
+  // Slot order: the first LEAD_U slots are U MFMAs, then T and U alternate,
+  // and the last LEAD_U slots are T MFMAs. The operands of the first AHEAD
+  // slots were read at the end of the wave's vector interval (K_j and V_{j-1}
+  // are both visible by then). T slot n is key block n % KB at k-step n / KB and U slot n is d
   // block n % DBLK at k-step n / DBLK, so consecutive MFMAs never share an
   // accumulator.
   constexpr int NPV = T::PSTEPS * T::DBLK;
@@ -466,20 +464,25 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     for (int m = i + 1; m <= i + AHEAD && m < NM; ++m) r += slot_is_u(m) ? 2 : 1;
     return r;
   };
-  static_assert(2 * AHEAD <= 15, "the wait count fits lgkmcnt");
+  static_assert([reads_after]() constexpr {
+    int m = 0;
+    for (int i = 0; i < NM; ++i) m = reads_after(i) > m ? reads_after(i) : m;
+    return m;
+  }() <= 15, "the wait count fits lgkmcnt");
   half8 ring[AHEAD];
-  // End of a vector interval: the lead U operands of the next matrix-core
-  // interval (U_j, V slot j % 4).
+  // End of a vector interval: the first AHEAD operands of the next
+  // matrix-core interval (U_j from V slot j % 4, T_{j+1} from K slot
+  // (j + 1) % 4), so that interval starts with its read-ahead ring full.
   auto prefetch_lead = [&](auto v_tag) __attribute__((always_inline)) {
+    constexpr int KN = (decltype(v_tag)::value + 1) % 4;
 #pragma unroll
-    for (int i = 0; i < LEAD_U; ++i) ring[i] = read_u(v_tag, i);
+    for (int i = 0; i < AHEAD; ++i)
+      ring[i] = slot_is_u(i) ? read_u(v_tag, slot_n(i)) : read_t(std::integral_constant<int, KN>{}, slot_n(i));
   };
   auto mfma_interval = [&](auto k_tag, auto v_tag) __attribute__((always_inline)) {
     auto operand = [&](int i) __attribute__((always_inline)) {
       return slot_is_u(i) ? read_u(v_tag, slot_n(i)) : read_t(k_tag, slot_n(i));
     };
-#pragma unroll
-    for (int i = LEAD_U; i < AHEAD; ++i) ring[i] = operand(i);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -503,31 +506,34 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // ---- ping-pong schedule -------------------------------------------------------
   // Every wave runs the same sequence of barrier-separated local intervals.
   // 2j is the matrix-core interval of iteration j: U_{j-1} and T_j. 2j+1 is
-  // the vector interval: the DMAs of K_{j+2} and V_{j+2}, C_j (mask, exp2,
-  // fp16 pack, row max, and when needed the lazy rescale), then the lead V
-  // operands of U_j. Group 1 starts one interval late (an extra barrier up
+  // the vector interval: the DMAs of K_{j+3} and V_{j+2}, C_j (mask, exp2,
+  // fp16 pack, row max, and when needed the lazy rescale), then the first
+  // operands of the next matrix-core interval. Group 1 starts one interval late (an extra barrier up
   // front, which group 0 matches at the end), so in every interval one wave
   // of each SIMD feeds the matrix core while the other runs the vector work.
   // Global interval = local interval + group.
   //
-  // Rings (slot = tile % 4). K_t and V_t are issued in local 2t-3 and waited
-  // for at the end of local 2t-2 (vmcnt(0): nothing is issued after them
-  // before local 2t-1); after the barrier ending global 2t-1 every wave's
-  // share has landed. K_t is read in global 2t .. 2t+1, V_t from global 2t+1
-  // (group 0's lead operands of U_t) to 2t+3. The next DMA into either slot
-  // (tile t+4) is issued in global 2t+5 or later. Loads past the sequence
+  // Rings (slot = tile % 4). K_t is issued in local 2t-5 and waited for at
+  // the end of local 2t-4; after the barrier ending global 2t-3 every wave's
+  // share has landed, and it is read from global 2t-1 (group 0's lead
+  // operands) to 2t+1. V_t is issued in local 2t-3 and waited for at the end
+  // of local 2t-2; visible after global 2t-1, it is read from global 2t+1 to
+  // 2t+3. Each wait is vmcnt(0): a vector interval issues K_{j+3} and
+  // V_{j+2}, and nothing more before the end of the next matrix-core
+  // interval. The next DMA into a K slot (tile t+4) is issued in global 2t+3
+  // or later, into a V slot in global 2t+5 or later. Loads past the sequence
   // end return zeros into slots that are never read.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
-    // this wave's K_{j+1} and V_{j+1} DMAs landed
+    // this wave's K_{j+2} and V_{j+1} DMAs landed
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto vector_sync = [&]() __attribute__((always_inline)) {
-    // this wave's lead operand reads are done
+    // this wave's operand reads for the next interval are done
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   auto produce = [&](int j) __attribute__((always_inline)) {
-    fetch_k(j + 2);
+    fetch_k(j + 3);
     fetch_v(j + 2);
   };
 
@@ -568,8 +574,9 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     fetch_k(0);
     fetch_v(0);
     fetch_k(1);
+    fetch_k(2);
     fetch_v(1);
-    // K_0 and V_0 landed in every wave (K_1 and V_1 may be in flight)
+    // K_0, V_0 and K_1 landed in every wave (K_2 and V_1 may be in flight)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * T::LOADS_PER_WAVE) : "memory");
     if (group == 1) sync();
 
@@ -648,19 +655,37 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // lanes q and q + 32 hold query q; the row sum sits in lane q (lane q + 32 has 0)
   const float l_tot = sum_halves(lacc[0]);
   const float inv = 1.f / l_tot;
-  if (qrow < N) {
-    _Float16* orow = p.o + head + (size_t)qrow * D;
+  // O goes through LDS (the rings are idle now) so that the global stores
+  // are whole rows: each wave writes its 32 rows of fp16 O into a region of
+  // its own, rows padded by 16 bytes (a 32-lane write of one d column then
+  // hits each bank at most twice, and the 16-byte row reads stay aligned and
+  // conflict-free), and stores 16 bytes per lane, D / 8 lanes per row.
+  constexpr int O_STRIDE = D * 2 + 16;
+  static_assert(T::WAVES * T::QW * O_STRIDE <= T::LDS_BYTES, "O staging fits the rings");
+  lds_char* const ob = k_ring + wave * T::QW * O_STRIDE;
 #pragma unroll
-    for (int b = 0; b < T::DBLK; ++b)
+  for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        half4 w = {(_Float16)(oacc[b][4 * g + 0] * inv), (_Float16)(oacc[b][4 * g + 1] * inv),
-                   (_Float16)(oacc[b][4 * g + 2] * inv), (_Float16)(oacc[b][4 * g + 3] * inv)};
-        *reinterpret_cast<half4*>(orow + 32 * b + 8 * g + 4 * hh) = w;
-      }
-    if (hh == 0)
-      p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    for (int g = 0; g < 4; ++g) {
+      // register 4g + e of block b is d = 32b + 8g + 4hh + e
+      half4 w = {(_Float16)(oacc[b][4 * g + 0] * inv), (_Float16)(oacc[b][4 * g + 1] * inv),
+                 (_Float16)(oacc[b][4 * g + 2] * inv), (_Float16)(oacc[b][4 * g + 3] * inv)};
+      *(__attribute__((address_space(3))) half4*)(ob + l32 * O_STRIDE + (32 * b + 8 * g + 4 * hh) * 2) = w;
+    }
+  constexpr int LANES_PER_ROW = D / 8;
+  constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
+  const int srow = lane / LANES_PER_ROW, scol = 8 * (lane % LANES_PER_ROW);
+#pragma unroll
+  for (int r0 = 0; r0 < T::QW; r0 += ROWS_PER_STORE) {
+    const int row = r0 + srow;
+    const half8 x = *(const __attribute__((address_space(3))) half8*)(ob + row * O_STRIDE + 2 * scol);
+    if (wave_q_lo + row < N) *reinterpret_cast<half8*>(p.o + head + (size_t)(wave_q_lo + row) * D + scol) = x;
   }
+  if (qrow < N && hh == 0)
+    p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  // the next tile's DMAs may refill the rings only once every wave has read
+  // its staged rows back
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int D, bool CAUSAL>
