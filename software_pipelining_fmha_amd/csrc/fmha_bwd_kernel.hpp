@@ -23,12 +23,13 @@
 // no workspace beyond D and lse is needed and results are deterministic; the
 // price is S and dP computed twice (7 matrix products instead of 5).
 //
-// Streamed tiles land in a two-slot LDS ring (the load of step t+1 is in
-// flight during the compute of step t) as [row][d] with 16-byte chunk c of
-// row r at chunk c ^ swz(r): through registers in the dK/dV kernel, by
-// LDS-DMA in the dQ kernel. One layout serves both reads: MFMA A operands of
-// whole rows (ds_read_b128) and transposed A operands (ds_read_b64_tr_b16,
-// 8 rows of one d column), both free of LDS bank conflicts.
+// Streamed tiles arrive by LDS-DMA (16 bytes per lane straight into LDS, no
+// register staging) as [row][d] with 16-byte chunk c of row r at chunk
+// c ^ swz(r): in four-slot rings two steps ahead in the dK/dV kernel, in a
+// two-slot ring one step ahead in the dQ kernel. One layout serves both
+// reads: MFMA A operands of whole rows (ds_read_b128) and transposed A
+// operands (ds_read_b64_tr_b16, 8 rows of one d column), both free of LDS
+// bank conflicts.
 #pragma once
 
 #include "fmha_fwd_kernel.hpp"
@@ -167,8 +168,12 @@ __device__ __forceinline__ int bwd_tile_id(int G) {
 // wave of each SIMD feeds the matrix core while the other runs vector work:
 //   interval A_t: P wave  MFMA  dV_{t-1}, S_t     | dS wave VALU dS_{t-1}
 //   interval B_t: P wave  VALU  P_t (to LDS)      | dS wave MFMA dK_{t-1}, dP_t
-// Streamed steps sit in a 3-slot ring: step t+1 is loaded into registers at
-// the start of step t and written to LDS during B_t.
+// The Q and dO tiles of a step and its two per-query statistics arrive by
+// LDS-DMA (no register staging) in four-slot rings, two steps ahead: the
+// tiles of step t + 2 are requested during step t and waited for (vmcnt) at
+// the end of step t + 1. A wave reads the first operands of its next
+// matrix-core interval at the end of its vector interval, so the matrix core
+// starts as soon as the barrier opens.
 template <int D>
 struct DkdvTile {
   static constexpr int WAVES = 8;
@@ -183,28 +188,52 @@ struct DkdvTile {
   static constexpr int DBLK = D / 32;
   static constexpr int CPR = D / 8;
   static constexpr int TILE_BYTES = BS * D * 2;
-  static constexpr int TILE_CHUNKS = TILE_BYTES / 16;
-  static constexpr int STAT_BYTES = 2 * BS * 4;
-  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + STAT_BYTES;
-  static constexpr int SLOTS = 3;
+  static constexpr int SLOTS = 4;
+  static constexpr int RING_BYTES = SLOTS * TILE_BYTES;
+  static constexpr int Q_RING = 0;               // Q tiles, one per slot
+  static constexpr int DO_RING = RING_BYTES;     // dO tiles
+  static constexpr int STAT_BYTES = 2 * BS * 4;  // per slot: D, then -lse * log2(e)
+  static constexpr int STATS = 2 * RING_BYTES;
   static constexpr int P_BYTES = QSTEPS * 1024;  // one pair's P (64 x 32 fp16)
-  static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES + PAIRS * P_BYTES;
-  // staging: CPT 16-byte chunks per thread for each of the two tiles
-  static constexpr int CPT = TILE_CHUNKS / THREADS;
-  static_assert(CPT >= 1 && CPT * THREADS == TILE_CHUNKS, "staging covers a step");
-  static_assert(2 * BS <= THREADS, "one thread per statistic");
+  static constexpr int PBUF = STATS + SLOTS * STAT_BYTES;
+  static constexpr int LDS_BYTES = PBUF + PAIRS * P_BYTES;
+  static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;  // wave-wide 16-byte-per-lane DMAs
+  static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;
+  // DMAs a wave issues per step: its share of both tiles and one statistic
+  static constexpr int DMA_PER_STEP = 2 * LOADS_PER_WAVE + 1;
+  static_assert(LOADS_PER_WAVE >= 1 && LOADS_PER_WAVE * WAVES == LOADS_PER_TILE, "tile DMAs split over the waves");
+  static_assert(BS == 64, "one wave-wide 4-byte DMA carries a step's statistic");
+  static_assert(RING_BYTES <= 65536, "ring offsets fit a DS instruction's immediate");
+  static_assert(DMA_PER_STEP <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
 };
+
+// LDS reads of the streaming loops are inline asm with explicit lgkmcnt
+// waits: as builtins, the compiler cannot tell that they miss the slots an
+// LDS-DMA is filling, and would wait for every DMA in flight before each.
+// Four 16-byte reads at a + O0 .. a + O3, waited for in the same block.
+template <int O0, int O1, int O2, int O3, typename V>
+__device__ __forceinline__ void lds_read4_wait(uint32_t a, V (&v)[4]) {
+  static_assert(sizeof(V) == 16, "16-byte reads");
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+      : "memory");
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(BwdParams p) {
   using T = DkdvTile<D>;
   typedef __attribute__((address_space(3))) char lds_char;
-  typedef __attribute__((address_space(3))) half8 lds_half8;
   typedef __attribute__((address_space(3))) intx4 lds_intx4;
-  typedef __attribute__((address_space(3))) floatx4 lds_floatx4;
   __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
   lds_char* const smem = (lds_char*)smem_raw;
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -225,8 +254,11 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
   const uint32_t head_bytes = (uint32_t)N * D * 2u;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.ws + (size_t)bh * N, (uint32_t)N * 4u);
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.ws + p.rows + (size_t)bh * N, (uint32_t)N * 4u);
+  // P waves bring each step's -lse * log2(e), dS waves its D (all four waves
+  // of a role write the same values)
+  const __amdgpu_buffer_rsrc_t rstat =
+      make_rsrc(p.ws + (p_wave ? (size_t)p.rows : 0) + (size_t)bh * N, (uint32_t)N * 4u);
+  const int stat_which = p_wave ? 1 : 0;
 
   // This wave's B operand rows: K (P wave) or V (dS wave) of its keys, lane
   // column = key, lane half hh holding d = 16 s + 8 hh .. +7.
@@ -242,55 +274,55 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
   for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
-
-  Offsets<D> off;
-  off.init(lane);
   const float c2 = p.scale_log2;
-
-  // staging of one step: CPT 16-byte chunks per thread of each of the Q and
-  // dO tiles, and the D and -lse*log2(e) values of its BS queries
-  int g_off[T::CPT], l_off[T::CPT];
-#pragma unroll
-  for (int c = 0; c < T::CPT; ++c) {
-    const int chunk = tid + T::THREADS * c;
-    const int crow = chunk / T::CPR, ccol = chunk % T::CPR;
-    g_off[c] = (crow * D + 8 * ccol) * 2;
-    l_off[c] = crow * D * 2 + 16 * (ccol ^ bwd_swz<D>(crow));
-  }
-  intx4 sa[T::CPT], sb[T::CPT];
-  float sst = 0.f;
-  auto stage_load = [&](int q_s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < T::CPT; ++c) {
-      sa[c] = load16(rq, q_s * D * 2 + g_off[c]);
-      sb[c] = load16(rdo, q_s * D * 2 + g_off[c]);
-    }
-    if (tid < 2 * T::BS)
-      sst = tid < T::BS ? load_f32(rD, (q_s + tid) * 4) : load_f32(rL, (q_s + tid - T::BS) * 4);
-  };
-  auto stage_store = [&](lds_char* sl) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < T::CPT; ++c) {
-      *(lds_intx4*)(sl + l_off[c]) = sa[c];
-      *(lds_intx4*)(sl + T::TILE_BYTES + l_off[c]) = sb[c];
-    }
-    if (tid < 2 * T::BS) *(__attribute__((address_space(3))) float*)(sl + 2 * T::TILE_BYTES + 4 * tid) = sst;
-  };
-  lds_char* const pbuf = smem + T::SLOTS * T::SLOT_BYTES + pair * T::P_BYTES;
 
   const int q_begin = CAUSAL ? k0 : 0;
   const int n_steps = (N - q_begin + T::BS - 1) / T::BS;
-  // a causal step entirely before the pair's first key contributes nothing
-  auto active = [&](int step) __attribute__((always_inline)) {
-    return step >= 0 && step < n_steps && (!CAUSAL || q_begin + step * T::BS + T::BS - 1 >= kw0);
-  };
-  // per-query statistic `which` (0: D, 1: -lse*log2(e)) of query block qb,
-  // as laid out in the accumulators: v[g][e] for register 4 g + e
-  auto stats = [&](const lds_char* sl, int which, int qb, floatx4 (&v)[4]) __attribute__((always_inline)) {
-    const lds_char* st = sl + 2 * T::TILE_BYTES + which * T::BS * 4 + qb * 32 * 4;
+
+  // ---- producer: step s into ring slot s % 4 --------------------------------
+  // Load i of a tile fills LDS chunks 64 i .. 64 i + 63, one per lane; chunk
+  // x = row * CPR + pos holds global chunk pos ^ swz(row) of that row (the
+  // swizzle is an involution on chunk indices). Steps past the last one read
+  // past the end of the head and land zeros; every wave issues exactly
+  // DMA_PER_STEP DMAs per step, so the vmcnt counts are fixed.
+  int src[T::LOADS_PER_WAVE];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) v[g] = *(const lds_floatx4*)(st + 4 * (16 * (g >> 1) + 8 * hh + 4 * (g & 1)));
+  for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+    const int x = 64 * (wave * T::LOADS_PER_WAVE + i) + lane;
+    const int row = x / T::CPR, pos = x % T::CPR;
+    src[i] = (row * D + 8 * (pos ^ bwd_swz<D>(row))) * 2;
+  }
+  auto fetch = [&](int step, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const int q_s = q_begin + step * T::BS;
+    const int wofs = wave * T::LOADS_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+      load16_to_lds(rq, q_s * D * 2 + src[i], smem + T::Q_RING + S * T::TILE_BYTES + wofs + i * 1024);
+      load16_to_lds(rdo, q_s * D * 2 + src[i], smem + T::DO_RING + S * T::TILE_BYTES + wofs + i * 1024);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rstat, smem + T::STATS + S * T::STAT_BYTES + stat_which * T::BS * 4,
+                                             4, (q_s + lane) * 4, 0, 0, 0);
   };
+
+  // ---- consumer-side LDS addresses (per lane; slot and block are immediates)
+  // The P wave reads Q as whole rows and dO transposed; the dS wave Q
+  // transposed and dO as whole rows.
+  Offsets<D> off;
+  off.init(lane);
+  const uint32_t nat_ring = sbase + (p_wave ? T::Q_RING : T::DO_RING);
+  const uint32_t tr_ring = sbase + (p_wave ? T::DO_RING : T::Q_RING);
+  uint32_t nat_rd[T::KSTEPS], tr_rd[T::DBLK][2];
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s) nat_rd[s] = nat_ring + off.nat[s];
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) tr_rd[b][rd] = tr_ring + off.tr[b][rd];
+  // statistics: query 32 qb + 16 (i / 8) + 8 hh + i % 8 of the step for
+  // accumulator register i; P of a pair: 1024 bytes per 16-query k-step
+  const uint32_t stat_rd = sbase + T::STATS + 4 * 8 * hh;
+  const uint32_t p_rw = sbase + T::PBUF + pair * T::P_BYTES + 16 * lane;
 
   // S (P wave) or dP (dS wave) of the newest step, per 32-query block: lane
   // = key, register i = query 32 qb + 16 (i / 8) + 8 hh + i % 8 of the step
@@ -299,34 +331,58 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
   // k-step: w16[2 qb + i / 8][i % 8] is register i of block qb
   half8 w16[T::QSTEPS];
 
-  // Matrix-core interval: acc += (tile ct of step t-1)^T w16 (DBLK x QSTEPS
-  // MFMAs), then sc = (tile rt of step t) bf (QB x KSTEPS), in a fixed order
-  // in which consecutive MFMAs of one kind alternate accumulators, each LDS
-  // operand read OPERAND_AHEAD MFMAs before its use. It always runs whole:
-  // w16 is zero when step t-1 contributes nothing (the ring starts zeroed, so
-  // its operands are finite), and sc is simply unused when step t is
+  // Matrix-core interval: acc += (transposed tile of step t-1)^T w16 (NC =
+  // DBLK x QSTEPS MFMAs), then sc = (row tile of step t) bf (QB x KSTEPS),
+  // in a fixed order in which consecutive MFMAs of one kind alternate
+  // accumulators. Operand i is read AHEAD MFMAs before its use (the first
+  // AHEAD by `prefetch`, before the interval's barrier), and MFMA i waits
+  // only for its own operand: LDS reads complete in order. It always runs
+  // whole: w16 is zero when step t-1 contributes nothing (the ring's
+  // previous slot holds finite values), and sc is unused when step t is
   // inactive.
-  auto mfma_interval = [&](const lds_char* cs, int ct, const lds_char* rs, int rt)
-      __attribute__((always_inline)) {
-    constexpr int NC = T::DBLK * T::QSTEPS, NM = NC + T::QB * T::KSTEPS, AHEAD = OPERAND_AHEAD;
-    const lds_char* csrc = cs + ct * T::TILE_BYTES;
-    const lds_char* rsrc = rs + rt * T::TILE_BYTES;
-    auto operand = [&](int i) __attribute__((always_inline)) {
-      if (i < NC) {
-        const int b = i % T::DBLK, ks = i / T::DBLK;
-        return tr_pair(csrc, off.tr[b][0] + ks * 16 * D * 2, off.tr[b][1] + ks * 16 * D * 2);
-      }
+  constexpr int NC = T::DBLK * T::QSTEPS, NM = NC + T::QB * T::KSTEPS, AHEAD = OPERAND_AHEAD;
+  static_assert(AHEAD <= NC, "the prefetched operands are all from the previous step's tile");
+  auto reads_of = [](int i) constexpr { return i < NC ? 2 : 1; };
+  auto reads_after = [reads_of](int i) constexpr {
+    int r = 0;
+    for (int m = i + 1; m < i + AHEAD && m < NM; ++m) r += reads_of(m);
+    return r;
+  };
+  static_assert(reads_after(0) <= 15 && reads_after(NC - AHEAD) <= 15, "lgkmcnt range");
+  auto operand = [&](auto ps_tag, auto cs_tag, int i) __attribute__((always_inline)) {
+    constexpr int PS = decltype(ps_tag)::value, CS = decltype(cs_tag)::value;
+    half8 a;
+    if (i < NC) {
+      const int b = i % T::DBLK, ks = i / T::DBLK;
+      shortx4 lo, hi;
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(lo)
+                   : "v"(tr_rd[b][0]), "i"(PS * T::TILE_BYTES + ks * 16 * D * 2));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(hi)
+                   : "v"(tr_rd[b][1]), "i"(PS * T::TILE_BYTES + ks * 16 * D * 2));
+      a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
       const int n = i - NC, qb = n % T::QB, k = n / T::QB;
-      return *(const lds_half8*)(rsrc + off.nat[k] + qb * 32 * D * 2);
-    };
-    half8 ring[AHEAD];
+      asm volatile("ds_read_b128 %0, %1 offset:%2"
+                   : "=v"(a)
+                   : "v"(nat_rd[k]), "i"(CS * T::TILE_BYTES + qb * 32 * D * 2));
+    }
+    return a;
+  };
+  half8 ring[AHEAD];
+  auto prefetch = [&](auto ps_tag) __attribute__((always_inline)) {
+    using C0 = std::integral_constant<int, 0>;
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) ring[i] = operand(i);
+    for (int i = 0; i < AHEAD; ++i) ring[i] = operand(ps_tag, C0{}, i);
+  };
+  auto mfma_interval = [&](auto ps_tag, auto cs_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const half8 a = ring[i % AHEAD];
-      if (i + AHEAD < NM) ring[i % AHEAD] = operand(i + AHEAD);
+      half8 a = ring[i % AHEAD];
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(reads_after(i)));
+      if (i + AHEAD < NM) ring[i % AHEAD] = operand(ps_tag, cs_tag, i + AHEAD);
       if (i < NC) {
         const int b = i % T::DBLK, ks = i / T::DBLK;
         acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, w16[ks], acc[b], 0, 0, 0);
@@ -344,30 +400,45 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) w16[k][i] = (_Float16)0.f;
   };
+  // per-query statistic `which` of query block qb, as laid out in the
+  // accumulators: v[g][e] for register 4 g + e
+  auto stats = [&](auto slot_tag, auto which_tag, auto qb_tag, floatx4 (&v)[4]) __attribute__((always_inline)) {
+    constexpr int O = decltype(slot_tag)::value * T::STAT_BYTES + decltype(which_tag)::value * T::BS * 4 +
+                      decltype(qb_tag)::value * 32 * 4;
+    lds_read4_wait<O, O + 16, O + 64, O + 80>(stat_rd, v);
+  };
 
-  // One step t in the role of this wave. Slot indices are compile-time (U is
-  // t mod 3), so LDS addresses are a lane register plus an immediate.
+  // a causal step entirely before the pair's first key contributes nothing
+  auto active = [&](int step) __attribute__((always_inline)) {
+    return step >= 0 && step < n_steps && (!CAUSAL || q_begin + step * T::BS + T::BS - 1 >= kw0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // One step t in the role of this wave; U = t mod 4 is compile-time, so
+  // every LDS address is a lane register plus an immediate.
   auto p_step = [&](int t, auto u_tag) __attribute__((always_inline)) {
     constexpr int U = decltype(u_tag)::value;
-    lds_char* const cur = smem + U * T::SLOT_BYTES;
-    lds_char* const prev = smem + ((U + 2) % 3) * T::SLOT_BYTES;
-    lds_char* const next = smem + ((U + 1) % 3) * T::SLOT_BYTES;
-    if (t + 1 < n_steps) stage_load(q_begin + (t + 1) * T::BS);
+    using PREV = std::integral_constant<int, (U + 3) % 4>;
+    using CUR = std::integral_constant<int, U>;
+    using FILL = std::integral_constant<int, (U + 2) % 4>;
     // interval A: dV^T += dO^T P (step t-1), then S = Q K^T (step t)
     __builtin_amdgcn_s_setprio(1);
-    mfma_interval(prev, 1, cur, 0);
+    mfma_interval(PREV{}, CUR{});
     __builtin_amdgcn_s_setprio(0);
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");
     // interval B: P = 2^(S c - lse log2 e) in fp16, to registers and LDS
     if (active(t)) {
       const int q_s = q_begin + t * T::BS;
       // base-2 exponents s c - lse log2 e (any finite scale)
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) {
+      {
         floatx4 nl[4];
-        stats(cur, 1, qb, nl);
+        stats(CUR{}, I1{}, I0{}, nl);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[qb][i] = __builtin_fmaf(sc[qb][i], c2, nl[i >> 2][i & 3]);
+        for (int i = 0; i < 16; ++i) sc[0][i] = __builtin_fmaf(sc[0][i], c2, nl[i >> 2][i & 3]);
+        stats(CUR{}, I1{}, I1{}, nl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[1][i] = __builtin_fmaf(sc[1][i], c2, nl[i >> 2][i & 3]);
       }
       // Masked exponents become -inf (weight 0), on edge steps only: the test
       // is uniform, so other steps branch past it.
@@ -386,78 +457,107 @@ __global__ __launch_bounds__(DkdvTile<D>::THREADS, 1) void fmha_bwd_dkdv_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           w16[2 * qb + (i >> 3)][i & 7] = (_Float16)__builtin_amdgcn_exp2f(sc[qb][i]);
-#pragma unroll
-      for (int k = 0; k < T::QSTEPS; ++k)
-        *(__attribute__((address_space(3))) half8*)(pbuf + 1024 * k + 16 * lane) = w16[k];
+      static_assert(T::QSTEPS == 4, "four 16-byte P writes per lane");
+      asm volatile(
+          "ds_write_b128 %0, %1\n\t"
+          "ds_write_b128 %0, %2 offset:1024\n\t"
+          "ds_write_b128 %0, %3 offset:2048\n\t"
+          "ds_write_b128 %0, %4 offset:3072"
+          :
+          : "v"(p_rw), "v"(w16[0]), "v"(w16[1]), "v"(w16[2]), "v"(w16[3])
+          : "memory");
     } else {
       zero_w16();
     }
-    if (t + 1 < n_steps) stage_store(next);
-    __syncthreads();
+    fetch(t + 2, FILL{});
+    // the next interval's first operands: dO of this step, transposed
+    if (t < n_steps) prefetch(CUR{});
+    // end of step: step t + 1's tiles have landed (only step t + 2's DMAs
+    // may be pending) and the P writes are done (issued before the
+    // prefetch's 2 AHEAD reads)
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(T::DMA_PER_STEP), "n"(2 * AHEAD) : "memory");
   };
   auto ds_step = [&](int t, auto u_tag) __attribute__((always_inline)) {
     constexpr int U = decltype(u_tag)::value;
-    lds_char* const cur = smem + U * T::SLOT_BYTES;
-    lds_char* const prev = smem + ((U + 2) % 3) * T::SLOT_BYTES;
-    lds_char* const next = smem + ((U + 1) % 3) * T::SLOT_BYTES;
-    if (t + 1 < n_steps) stage_load(q_begin + (t + 1) * T::BS);
+    using PREV = std::integral_constant<int, (U + 3) % 4>;
+    using CUR = std::integral_constant<int, U>;
+    using FILL = std::integral_constant<int, (U + 2) % 4>;
+    fetch(t + 2, FILL{});
     // interval A: dS = P (dP - D) of step t-1, P from the P wave
     if (active(t - 1)) {
+      half8 pw[4];
+      lds_read4_wait<0, 1024, 2048, 3072>(p_rw, pw);
 #pragma unroll
       for (int qb = 0; qb < T::QB; ++qb) {
         floatx4 dd[4];
-        stats(prev, 0, qb, dd);
-        const half8 p0 = *(const lds_half8*)(pbuf + 1024 * (2 * qb) + 16 * lane);
-        const half8 p1 = *(const lds_half8*)(pbuf + 1024 * (2 * qb + 1) + 16 * lane);
+        if (qb == 0) stats(PREV{}, I0{}, I0{}, dd);
+        else stats(PREV{}, I0{}, I1{}, dd);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+          const float pv = (float)pw[2 * qb + (i >> 3)][i & 7];
           w16[2 * qb + (i >> 3)][i & 7] = (_Float16)(pv * (sc[qb][i] - dd[i >> 2][i & 3]));
         }
       }
     } else {
       zero_w16();
     }
-    __syncthreads();
+    // interval B's first operands: Q of step t-1, transposed
+    prefetch(PREV{});
+    asm volatile("s_barrier" ::: "memory");
     // interval B: dK^T += Q^T dS (step t-1), then dP = dO V^T (step t)
     __builtin_amdgcn_s_setprio(1);
-    mfma_interval(prev, 0, cur, 1);
+    mfma_interval(PREV{}, CUR{});
     __builtin_amdgcn_s_setprio(0);
-    if (t + 1 < n_steps) stage_store(next);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::DMA_PER_STEP) : "memory");
   };
   using U0 = std::integral_constant<int, 0>;
   using U1 = std::integral_constant<int, 1>;
   using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
 
-  // prologue: the ring zeroed, then step 0 staged into slot 0
-  stage_load(q_begin);
-  for (int x = tid; x < T::SLOTS * T::SLOT_BYTES / 16; x += T::THREADS)
-    *(lds_intx4*)(smem + 16 * x) = intx4{0, 0, 0, 0};
-  __syncthreads();
-  stage_store(smem);
+  // prologue: slot 3 (step 0's "previous" slot) zeroed, steps 0 and 1
+  // requested, step 0 waited for
+  for (int x = tid; x < T::TILE_BYTES / 16; x += T::THREADS) {
+    *(lds_intx4*)(smem + T::Q_RING + 3 * T::TILE_BYTES + 16 * x) = intx4{0, 0, 0, 0};
+    *(lds_intx4*)(smem + T::DO_RING + 3 * T::TILE_BYTES + 16 * x) = intx4{0, 0, 0, 0};
+  }
+  fetch(0, U0{});
+  fetch(1, U1{});
   zero_w16();
-  __syncthreads();
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::DMA_PER_STEP) : "memory");
+  // bf (loaded before the DMAs) has landed too; passing it through an empty
+  // asm tells the compiler so, which keeps it from waiting for every DMA in
+  // flight before the loop
+#pragma unroll
+  for (int s = 0; s < T::KSTEPS; ++s) asm volatile("" : "+v"(bf[s]));
   // steps 0 .. n_steps (the last one only finishes step n_steps - 1)
   if (p_wave) {
+    prefetch(U3{});
     int t = 0;
-    for (; t + 2 <= n_steps; t += 3) {
+    for (; t + 3 <= n_steps; t += 4) {
       p_step(t, U0{});
       p_step(t + 1, U1{});
       p_step(t + 2, U2{});
+      p_step(t + 3, U3{});
     }
     if (t <= n_steps) p_step(t, U0{});
     if (t + 1 <= n_steps) p_step(t + 1, U1{});
+    if (t + 2 <= n_steps) p_step(t + 2, U2{});
   } else {
     int t = 0;
-    for (; t + 2 <= n_steps; t += 3) {
+    for (; t + 3 <= n_steps; t += 4) {
       ds_step(t, U0{});
       ds_step(t + 1, U1{});
       ds_step(t + 2, U2{});
+      ds_step(t + 3, U3{});
     }
     if (t <= n_steps) ds_step(t, U0{});
     if (t + 1 <= n_steps) ds_step(t + 1, U1{});
+    if (t + 2 <= n_steps) ds_step(t + 2, U2{});
   }
+  // the DMAs of the two steps past the end must land before the workgroup's
+  // LDS is released
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   // epilogue: register i of block b holds d = 32 b + 16 (i / 8) + 8 hh + i % 8
   if (key < N) {
