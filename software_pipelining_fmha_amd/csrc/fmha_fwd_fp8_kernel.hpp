@@ -249,6 +249,31 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
     }
   };
+  // Fast-pass split of exp_pack: in the vector interval, key block 0's
+  // weights are packed and block 1's are left in place in sacc[1] as fp32;
+  // the matrix-core interval packs them (cvt_hi) while its first two MFMAs,
+  // which rewrite only sacc[0], run. The packed bytes are the same.
+  auto exp_pack_lo = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = 4 * w;
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i + u], c2, -m_run));
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], c2, -m_run));
+  };
+  auto cvt_hi = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 4; w < 8; ++w) {
+      const int i = 4 * (w & 3);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[1][i], sacc[1][i + 1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[1][i + 2], sacc[1][i + 3], x, true);
+    }
+  };
   auto tile_max = [&]() __attribute__((always_inline)) {
     float t[11];
 #pragma unroll
@@ -282,10 +307,17 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       exp_pack();
     }
   };
-  // Fast C stage: weights against the fixed reference, no row max.
+  // Fast C stage: weights against the fixed reference, no row max; block
+  // 1's weights are packed in the next matrix-core interval.
   auto softmax_fast = [&](int j) __attribute__((always_inline)) {
     mask_tile(j);
-    exp_pack();
+    exp_pack_lo();
+  };
+  // Tile 0 of the fast pass: the reference is the tile's row max.
+  auto softmax_first_fast = [&]() __attribute__((always_inline)) {
+    mask_tile(0);
+    m_run = tile_max();
+    exp_pack_lo();
   };
   // T stage alone (tile 0): S^T = K_0 Q^T.
   auto qk = [&]() __attribute__((always_inline)) {
@@ -297,34 +329,42 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     }
   };
   // U stage alone (last tile of a wave).
-  auto pv = [&](int j) __attribute__((always_inline)) {
+  auto pv = [&](int j, auto split_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(split_tag)::value) cvt_hi();
     const lds_char* vs = v_ring + (j % T::SLOTS) * T::TILE_BYTES;
 #pragma unroll
     for (int b = 0; b < T::DBLK; ++b) oacc[b] = mfma_fp8(v_operand(vs, b), pf, oacc[b]);
     lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones_a, pf, lacc, 0, 0, 0, 127, 0, 127);
   };
-  // Matrix-core interval of iteration j: U_{j-1} and T_j alternating, then
-  // the row sum of P_{j-1}. Each operand is read AHEAD MFMAs before its use.
-  // The reads are inline asm: the compiler would otherwise wait for every
-  // LDS-DMA in flight (vmcnt(0)) before them, though none targets the slots
-  // read here. Their completion is waited for explicitly: LDS reads finish in
-  // order, so before MFMA i only the reads of operands i+1 .. i+AHEAD may be
-  // outstanding.
-  auto mfma_interval = [&](auto u_tag) __attribute__((always_inline)) {
+  // Matrix-core interval of iteration j: U_{j-1} and T_j, then the row sum
+  // of P_{j-1}. Exact pass: U and T alternate. Fast pass (SPLIT): T_j's two
+  // MFMAs of key block 0 first, then the packing of P_{j-1}'s block 1
+  // (cvt_hi), then the four U MFMAs and T_j's block 1. Each operand is read
+  // AHEAD MFMAs before its use. The reads are inline asm: the compiler would
+  // otherwise wait for every LDS-DMA in flight (vmcnt(0)) before them, though
+  // none targets the slots read here. Their completion is waited for
+  // explicitly: LDS reads finish in order, so before MFMA i only the reads
+  // of operands i+1 .. i+AHEAD may be outstanding.
+  auto mfma_interval = [&](auto u_tag, auto split_tag) __attribute__((always_inline)) {
     constexpr int U = decltype(u_tag)::value;
+    constexpr bool SPLIT = decltype(split_tag)::value;
     constexpr int PREV = (U + T::SLOTS - 1) % T::SLOTS;
     constexpr int NPV = T::DBLK, NT = T::KB * T::KSTEPS;
-    static_assert(NPV == NT, "U and T MFMAs alternate");
+    static_assert(NPV == 4 && NT == 4, "four U and four T MFMAs");
     constexpr int NM = NPV + NT, AHEAD = 2;
     constexpr int K_OFF = U * T::TILE_BYTES;
     constexpr int V_OFF = T::SLOTS * T::TILE_BYTES + PREV * T::TILE_BYTES;
     const uint32_t base = (uint32_t)(uintptr_t)k_ring;
-    auto reads = [](int i) constexpr { return (i & 1) == 0 ? T::RUNS : 2; };
+    // slot i: a U MFMA (d block idx(i)) or a T MFMA (n = idx(i): key block
+    // n / 2, k-step n % 2)
+    auto is_u = [](int i) constexpr { return SPLIT ? (i >= 2 && i < 6) : (i & 1) == 0; };
+    auto idx = [](int i) constexpr { return SPLIT ? (i < 2 ? i : (i < 6 ? i - 2 : i - 4)) : i >> 1; };
+    auto reads = [is_u](int i) constexpr { return is_u(i) ? T::RUNS : 2; };
     auto operand = [&](auto i_tag) __attribute__((always_inline)) {
       constexpr int i = decltype(i_tag)::value;
-      constexpr int n = i >> 1;
+      constexpr int n = idx(i);
       intx8 r;
-      if constexpr ((i & 1) == 0) {
+      if constexpr (is_u(i)) {
         intx2 x[T::RUNS];
 #pragma unroll
         for (int rho = 0; rho < T::RUNS; ++rho)
@@ -351,16 +391,20 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       if constexpr (i + AHEAD < NM) ring[i % AHEAD] = operand(std::integral_constant<int, i + AHEAD>{});
       constexpr int after = (i + 1 < NM ? reads(i + 1) : 0) + (i + 2 < NM ? reads(i + 2) : 0);
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(after));
-      constexpr int n = i >> 1;
+      constexpr int n = idx(i);
       // the empty asm keeps each MFMA in this interval (LLVM would sink the
       // U MFMAs, whose results are not needed until the next interval)
-      if constexpr ((i & 1) == 0) {
+      if constexpr (is_u(i)) {
         oacc[n] = mfma_fp8(a, pf, oacc[n]);
         asm volatile("" : "+v"(oacc[n]));
       } else {
         constexpr int kb = n >> 1, st = n & 1;
         sacc[kb] = mfma_fp8(a, qf[st], st == 0 ? floatx16{} : sacc[kb]);
         asm volatile("" : "+v"(sacc[kb]));
+      }
+      if constexpr (SPLIT && i == 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        cvt_hi();
       }
     };
     step(std::integral_constant<int, 0>{});
@@ -396,7 +440,7 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
   };
   auto steady = [&](int j, auto u_tag, auto exact_tag) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    mfma_interval(u_tag);
+    mfma_interval(u_tag, std::integral_constant<bool, !decltype(exact_tag)::value>{});
     __builtin_amdgcn_s_setprio(0);
     mfma_sync();
     produce_issue(j);
@@ -423,7 +467,10 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     if (n_wave > 0) qk();
     mfma_sync();
     produce_issue(0);
-    if (n_wave > 0) softmax(0);
+    if (n_wave > 0) {
+      if constexpr (decltype(exact_tag)::value) softmax(0);
+      else softmax_first_fast();
+    }
     vector_sync();
     int j = 1;
     for (; j + 4 <= n_wave; j += 4) {
@@ -447,7 +494,7 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     // n_wave <= j <= n_kv: the last U for this wave, then idle intervals in
     // which the wave still loads its share of the workgroup's tiles
     for (; j <= n_kv; ++j) {
-      if (j == n_wave && j >= 1) pv(j - 1);
+      if (j == n_wave && j >= 1) pv(j - 1, std::integral_constant<bool, !decltype(exact_tag)::value>{});
       mfma_sync();
       produce_issue(j);
       vector_sync();
