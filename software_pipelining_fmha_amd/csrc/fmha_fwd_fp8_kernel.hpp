@@ -10,8 +10,8 @@
 //   exponent reference stays at key tile 0's row max (no row max
 //   afterwards). The weights are rounded to E4M3, whose conversion turns
 //   values from 480 up into NaN (there is no infinity), so a fast-pass
-//   overflow shows as a NaN row sum and the tile reruns exactly. Each
-//   workgroup picks the pass from what its first tile shows (Fp8Pass);
+//   overflow shows as a NaN row sum and the tile reruns exactly. The choice
+//   is made per tile, from that tile's own data only;
 // - U stage, O^T += V^T P^T: one MFMA per 32-row block of d per 64-key tile.
 // Row sums of the E4M3 weights run on v_mfma_scale_f32_16x16x128_f8f6f4 with
 // a 0/1 A operand, so O is normalised by exactly the weights that multiply V.
@@ -87,18 +87,15 @@ __device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// The workgroup's choice of pass, kept across its tiles. E4M3's range is
-// small (weights overflow past about 2^8.9 of the reference), so inputs with
-// sharp softmax rows overflow the fast pass on most tiles, and a fast pass
-// plus a rerun costs more than the exact pass alone. So a fast tile that
-// overflows reruns exactly and switches the workgroup to the exact pass for
-// the rest of the launch. The causal kernel holds the exact pass only: with
-// both passes compiled in, its exact pass ran 5% slower on sharp inputs.
-enum Fp8Pass { FP8_FAST = 1, FP8_EXACT = 2 };
-
+// Pass choice. Every non-causal tile starts with the fast pass and reruns
+// with the exact one when a weight overflowed, so a tile's output bits
+// depend only on its own inputs (not on which tiles its workgroup ran
+// before). E4M3's range is small (weights overflow past about 2^8.9 of the
+// reference), so on sharp softmax rows most tiles pay for both passes. The
+// causal kernel holds the exact pass only: with both passes compiled in, its
+// exact pass ran 5% slower on sharp inputs.
 template <bool CAUSAL>
-__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw,
-                                             int& pass) {
+__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw) {
   using T = Fp8Tile;
   constexpr int D = T::D;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -518,7 +515,7 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     return any != 0;
   };
-  if (!CAUSAL && pass == FP8_FAST) {
+  if (!CAUSAL) {
     run_pipeline(std::integral_constant<bool, CAUSAL>{});
     // A weight that overflowed E4M3 is NaN, and so is its row sum.
     if (any_wave(!(sum_halves(lacc[0]) < INFINITY))) {
@@ -527,7 +524,6 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       lacc = floatx4{};
       m_run = -INFINITY;
       run_pipeline(std::true_type{});
-      pass = FP8_EXACT;
     }
   } else {
     run_pipeline(std::true_type{});
@@ -560,11 +556,10 @@ __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Pa
   const int G = p.total_wg;
   const int per = G >> 3, rem = G & 7;
   const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
-  int pass = CAUSAL ? FP8_EXACT : FP8_FAST;
   for (int r = 0; r * (int)gridDim.x < G; ++r) {
     const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
     if (tile >= G) break;
-    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw, pass);
+    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw);
   }
 }
 
