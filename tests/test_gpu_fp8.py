@@ -335,6 +335,18 @@ def test_fp8_deterministic_bitwise(device):
     assert np.array_equal(a1[1].view(np.uint32), a2[1].view(np.uint32))
 
 
+def test_fp8_causal_workload_repeats_bitwise(device):
+    """Three launches of the causal FP8 workload at full size give the same
+    bits (a race between waves would show as run-to-run differences)."""
+    idx = [i for i, w in enumerate(inputs.FP8_WORKLOADS) if w.causal][0]
+    b, sc, scale = inputs.fp8_workload_inputs(idx)
+    a1 = run(b, sc, True, scale)
+    for _ in range(2):
+        a2 = run(b, sc, True, scale)
+        assert np.array_equal(a1[0].view(np.uint16), a2[0].view(np.uint16))
+        assert np.array_equal(a1[1].view(np.uint32), a2[1].view(np.uint32))
+
+
 def test_fp8_guard_bands_untouched(device):
     import torch
     B, H, N, d = 1, 2, 333, 128
