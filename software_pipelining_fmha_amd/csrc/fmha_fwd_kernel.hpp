@@ -616,8 +616,10 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
       vector_sync();
     }
     if (group == 0) sync();
-    // no load may still be in flight when the workgroup exits
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Every wave's trailing DMAs (tiles past the end, zeros) have landed once
+    // all waves pass this barrier: the epilogue and the rerun check reuse the
+    // rings, across the waves' shares, right after it.
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   };
   // The causal kernel holds the exact pass only: with the fast pass and its
   // rerun compiled in as well, it ran 10% slower on a causal workload with
@@ -631,9 +633,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     // reruns with the row max and lazy rescale (the rings are idle here).
     const float l_fast = sum_halves(lacc[0]);
     const bool bad = __builtin_amdgcn_ballot_w64(!(l_fast < INFINITY)) != 0;
-    // the flags sit in the V ring, which trailing DMAs of other waves may
-    // still be writing until every wave has passed its vmcnt(0)
-    sync();
+    // the flags sit in the V ring (no DMA is in flight any more)
     __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)v_ring;
     if (lane == 0) flags[wave] = bad ? 1 : 0;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
