@@ -708,6 +708,47 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
   const int k_end = CAUSAL ? min(N, q0 + T::BT) : N;
   const int n_steps = (k_end + T::BS - 1) / T::BS;
 
+  // LDS operand addresses: a lane register plus an immediate (slot, tile,
+  // key block or k-step). Row operands of S^T = K Q^T and dP^T = V dO^T
+  // (K or V row key_of_row(l32) of the 32-key block, d = 16 k + 8 hh ..),
+  // and the transposed K operand of dQ^T += K^T dS^T.
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  uint32_t nat_rd[T::KSTEPS], tr_rd[T::DBLK][2];
+#pragma unroll
+  for (int k = 0; k < T::KSTEPS; ++k) nat_rd[k] = sbase + off.nat[k];
+#pragma unroll
+  for (int b = 0; b < T::DBLK; ++b)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) tr_rd[b][rd] = sbase + off.tr[b][rd];
+  // S/dP MFMA i: k-step i / 4, key block (i / 2) % 2, K (even i) or V (odd
+  // i); dQ MFMA i: k-step i / DBLK over the step's keys, d block i % DBLK.
+  // Consecutive MFMAs never share an accumulator. Each operand is read
+  // AHEAD MFMAs before its use and waited for alone (LDS reads complete in
+  // order); the reads are inline asm for the reason given at tr_block4.
+  constexpr int NSD = 4 * T::KSTEPS, NDQ = 4 * T::DBLK, AHEAD = OPERAND_AHEAD;
+  static_assert(T::KB == 2 && NSD >= AHEAD && NDQ >= AHEAD, "interval shapes");
+  auto sd_operand = [&](auto slot_tag, int i) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    const int k = i >> 2, kb = (i >> 1) & 1, is_v = i & 1;
+    half8 a;
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(a)
+                 : "v"(nat_rd[k]), "i"(SLOT * T::SLOT_BYTES + is_v * T::TILE_BYTES + kb * 32 * D * 2));
+    return a;
+  };
+  auto dq_operand = [&](auto slot_tag, int i) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    const int ks = i / T::DBLK, b = i % T::DBLK;
+    shortx4 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(lo)
+                 : "v"(tr_rd[b][0]), "i"(SLOT * T::SLOT_BYTES + ks * 16 * D * 2));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi)
+                 : "v"(tr_rd[b][1]), "i"(SLOT * T::SLOT_BYTES + ks * 16 * D * 2));
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   // One step: wait until this wave's part of tile `step` has landed, then a
   // barrier (every part has landed, and every wave is done with the other
   // slot); start the next tile's DMA into the other slot; compute.
@@ -715,24 +756,27 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (step + 1 < n_steps) fetch(step + 1, nxt_tag);
     const int k_s = step * T::BS;
-    const lds_char* sk = smem + decltype(cur_tag)::value * T::SLOT_BYTES;
-    const lds_char* sv = sk + T::TILE_BYTES;
     if (CAUSAL && k_s > qw0 + T::RW - 1) return;  // every key of the step is after every query
     // S^T = K Q^T and dP^T = V dO^T per 32-key block: lane = query, register
     // i = key k_s + 32 kb + 16 (i / 8) + 8 hh + i % 8.
     floatx16 s[T::KB], dp[T::KB];
+    half8 ring[AHEAD];
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
+    for (int i = 0; i < AHEAD; ++i) ring[i] = sd_operand(cur_tag, i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
+    for (int i = 0; i < NSD; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      half8 a = ring[i % AHEAD];
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(NSD - 1 - i < AHEAD - 1 ? NSD - 1 - i : AHEAD - 1));
+      if (i + AHEAD < NSD) ring[i % AHEAD] = sd_operand(cur_tag, i + AHEAD);
+      const int k = i >> 2, kb = (i >> 1) & 1;
+      if (i & 1) dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dof[k], k == 0 ? floatx16{} : dp[kb], 0, 0, 0);
+      else s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[k], k == 0 ? floatx16{} : s[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the dQ interval's first operands land during the vector work
 #pragma unroll
-    for (int k = 0; k < T::KSTEPS; ++k)
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        const int o = off.nat[k] + kb * 32 * D * 2;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sk + o), qf[k], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const lds_half8*)(sv + o), dof[k], dp[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < AHEAD; ++i) ring[i] = dq_operand(cur_tag, i);
     // base-2 exponents s c - lse log2 e (any finite scale)
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -759,16 +803,17 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
         dsf[2 * kb + (i >> 3)][i & 7] = (_Float16)(pv * (dp[kb][i] - Dq));
       }
     // dQ^T += K^T dS^T (k = keys, 16 per k-step)
-    static_assert(2 * T::KB == 4, "one transposed-read block covers the step's keys");
-    const uint32_t skb = (uint32_t)(uintptr_t)sk;
+    static_assert(2 * T::KB == 4, "four 16-key k-steps per step");
 #pragma unroll
-    for (int b = 0; b < T::DBLK; ++b) {
-      half8 a[4];
-      tr_block4<16 * D * 2>(skb + off.tr[b][0], skb + off.tr[b][1], a);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dqt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], dsf[ks], dqt[b], 0, 0, 0);
+    for (int i = 0; i < NDQ; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      half8 a = ring[i % AHEAD];
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(2 * (NDQ - 1 - i < AHEAD - 1 ? NDQ - 1 - i : AHEAD - 1)));
+      if (i + AHEAD < NDQ) ring[i % AHEAD] = dq_operand(cur_tag, i + AHEAD);
+      const int ks = i / T::DBLK, b = i % T::DBLK;
+      dqt[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsf[ks], dqt[b], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   using Slot0 = std::integral_constant<int, 0>;
   using Slot1 = std::integral_constant<int, 1>;
