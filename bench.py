@@ -149,6 +149,12 @@ def cpu_baseline(q, k, v, w, scale, o_gpu, lse_gpu, target_s: float):
     b, h, i = rows0.T
     err_o = float(np.abs(o_gpu[b, h, i].astype(np.float64) - o_ref).max())
     err_l = float(np.abs(lse_gpu[b, h, i].astype(np.float64) - l_ref).max())
+    # the same rows on one thread
+    t0 = time.perf_counter()
+    oracle.fmha_rows(q, k, v, rows0, causal=w.causal, scale=scale, threads=1)
+    t_one = time.perf_counter() - t0
+    vis0 = (rows0[:, 2] + 1).astype(np.float64) if w.causal else np.full(len(rows0), float(w.N))
+    flops0 = float((4.0 * w.d * vis0).sum())
 
     # grow the sample to about target_s seconds of oracle work
     n = int(min(w.B * w.H * w.N, max(len(rows0), len(rows0) * target_s / max(t_first, 1e-3))))
@@ -163,6 +169,8 @@ def cpu_baseline(q, k, v, w, scale, o_gpu, lse_gpu, target_s: float):
         "sample": "%d seeded (b,h,i) rows of %s, every visible key per row; %.1f s wall"
                   % (len(rows), w.name, dt),
         "seconds": dt,
+        "single_thread": {"value": flops0 / t_one / 1e12, "unit": "TFLOPS",
+                          "sample": "the %d parity rows; %.1f s wall" % (len(rows0), t_one)},
     }, {"rows": int(len(rows0)), "max_abs_o": err_o, "max_abs_lse": err_l,
         "pass": bool(err_o <= 2e-3 and err_l <= 1e-3)}
 
