@@ -577,8 +577,10 @@ def copy_calibration(mib: int, steps: int) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 100 for --pass gemm)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 5; 50 for --pass gemm)")
     ap.add_argument("--workload", default=inputs.WORKLOADS[inputs.HEADLINE].name,
                     choices=[w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.FP8_WORKLOADS]
                     + [w.name for w in inputs.GEMM_WORKLOADS])
@@ -599,6 +601,12 @@ def main(argv=None) -> int:
                     help="instead of attention, run a plain device copy of this many MiB "
                          "per step (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args(argv)
+    # A GEMM launch takes about 1 ms: the clocks need some 50 of them to
+    # settle, and the default 5 + 20 would time the ramp.
+    if args.steps is None:
+        args.steps = 100 if args.which == "gemm" else 20
+    if args.warmup is None:
+        args.warmup = 50 if args.which == "gemm" else 5
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the attention forward pass here is a "

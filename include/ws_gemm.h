@@ -43,8 +43,8 @@ extern "C" {
  * trace   : NULL, or a device buffer of ws_gemm_trace_words(...) 64-bit
  *           words that receives per-stage timestamps (100 MHz wall clock):
  *           per workgroup, (S + 1) rows of 5 words. Row i < S: DMA wave
- *           starts issuing stage i; stage i landed and signalled; MATH wave
- *           0 starts stage i; MATH wave 0 releases its slot; MATH wave 0's
+ *           0 starts issuing stage i; its share of stage i landed and
+ *           signalled; MATH wave 0 starts stage i; MATH wave 0 releases its slot; MATH wave 0's
  *           MFMAs of stage i have finished (a traced launch waits for them
  *           each stage). Row S: the workgroup's start, its end, its tile
  *           id, 0, 0.
@@ -53,7 +53,7 @@ extern "C" {
  *           gives up after about 2^22 polls, far beyond any legitimate wait.
  * stream  : hipStream_t (NULL = default stream).
  *
- * One workgroup (one DMA wave, four MATH waves) per output tile, at most
+ * One workgroup (four DMA waves, four MATH waves) per output tile, at most
  * one per CU. The call allocates nothing, is asynchronous and thread-safe.
  * Buffers are caller-owned device memory; c must not overlap a or b.
  * Limits (else status 2): 16-byte aligned a, b, c; (M + 256) * K * 2 and

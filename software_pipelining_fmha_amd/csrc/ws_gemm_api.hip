@@ -21,7 +21,7 @@ struct Variant {
 };
 
 // Every (T_M, T_N, T_K, ring) whose ring fits the LDS and whose tile loads
-// fit the DMA wave's vmcnt range.
+// fit each DMA wave's vmcnt range.
 #define WS_VARIANTS(X)                                                                        \
   X(64, 64, 64, 1) X(64, 64, 64, 2) X(64, 64, 64, 3) X(64, 64, 64, 4) X(64, 64, 128, 1)       \
   X(64, 64, 128, 2) X(64, 64, 128, 3) X(64, 64, 128, 4) X(64, 128, 64, 1) X(64, 128, 64, 2)   \
@@ -165,15 +165,15 @@ extern "C" void ws_model_default(ws_model_params* p, int cus) {
   // Two-point calibration on MI355X from the kernel's own stage trace, at
   // ring depth 1 so that loads and MATH never overlap: tiles 64x64x64 on
   // 1024^3 and 128x128x128 on 2048x2048x1024, each filling every CU once.
-  // Load per stage 0.319 and 1.166 us, MATH 0.354 and 0.974 us, epilogue
-  // 0.238 and 1.726 us (the constant is their mean), launch minus the traced
-  // span 4.21 and 4.72 us (mean).
-  p->load_throughput = 29027.0;  // elements per us, A and B together
-  p->load_latency = 0.0183;
-  p->compute_throughput = 2.957e6;  // multiply-adds per us
-  p->compute_latency = 0.265;
-  p->t_epilogue = 0.982;
-  p->t_init = 4.462;
+  // Load per stage 0.242 and 0.727 us, MATH 0.345 and 0.897 us, epilogue
+  // 0.234 and 1.793 us (the constant is their mean), launch minus the traced
+  // span 4.16 and 5.08 us (mean).
+  p->load_throughput = 50617.0;  // elements per us, A and B together
+  p->load_latency = 0.0400;
+  p->compute_throughput = 3.3269e6;  // multiply-adds per us
+  p->compute_latency = 0.2665;
+  p->t_epilogue = 1.013;
+  p->t_init = 4.617;
   p->n_units = cus > 0 ? cus : 256;
 }
 

@@ -122,7 +122,7 @@ def test_ring_depth_does_not_change_bits(device):
 @pytest.mark.parametrize("cfg", [(128, 128, 64, 1), (128, 128, 64, 3), (64, 64, 128, 2),
                                  (128, 128, 128, 2)], ids=lambda c: "t%dx%dx%d_r%d" % c)
 def test_trace_obeys_the_semaphores(cfg, device):
-    """Per workgroup and stage i: the DMA wave issues a stage before it
+    """Per workgroup and stage i: DMA wave 0 issues a stage before it
     lands, MATH wave 0 starts it after it landed, releases it after it
     started and finishes its MFMAs after that; stage i is issued only after
     stage i - ring was released (by MATH wave 0 at least)."""
