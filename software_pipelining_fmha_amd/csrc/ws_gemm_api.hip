@@ -188,8 +188,10 @@ extern "C" int ws_gemm_choose(const ws_model_params* p, int M, int N, int K, int
   // Smallest predicted time. Equal predictions (within rounding) go to the
   // deeper ring of the same tile: once the model has a ring hide the loads
   // fully, deeper rings predict the same time, while on the GPU they absorb
-  // the load-time spread that the model does not represent. Variants are
-  // listed with the ring depth ascending within each tile.
+  // the load-time spread that the model does not represent. That holds up
+  // to S = ceil(K / T_K) slots, as many as there are stages: a deeper ring
+  // never fills, and on the GPU it measured slower (its larger LDS block).
+  // Variants are listed with the ring depth ascending within each tile.
   int best = -1;
   double best_t = 0.0;
   for (int i = 0; i < N_VARIANTS; ++i) {
@@ -198,7 +200,7 @@ extern "C" int ws_gemm_choose(const ws_model_params* p, int M, int N, int K, int
     if (t < 0) continue;
     const bool deeper_tie = best >= 0 && v.tm == VARIANTS[best].tm && v.tn == VARIANTS[best].tn &&
                             v.tk == VARIANTS[best].tk && v.ring > VARIANTS[best].ring &&
-                            t <= best_t * (1.0 + 1e-9);
+                            v.ring <= cdiv(K, v.tk) && t <= best_t * (1.0 + 1e-9);
     if (best < 0 || t < best_t * (1.0 - 1e-9) || deeper_tie) {
       best = i;
       best_t = t;

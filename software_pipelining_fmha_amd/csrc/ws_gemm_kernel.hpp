@@ -86,6 +86,11 @@ struct GemmTile {
   static constexpr int KSTEPS = TK / 16;   // MFMA k-steps per stage
   static constexpr int CA = TK / 8;        // 16-byte chunks per A tile row
   static constexpr int CB = TN / 8;        // 16-byte chunks per B tile row
+  // A tile: chunk c of row r sits at chunk c ^ a_swz(r). ds_read_b128 serves
+  // 16 lanes (16 consecutive rows, one chunk) per pass, and the LDS banks
+  // span 256 bytes: with 128-byte rows, rows r and r + 8 share banks unless
+  // the swizzle differs across them, so it follows r / 2 there.
+  static constexpr __device__ __host__ int a_swz(int r) { return CA == 8 ? (r >> 1) & 7 : r & 15; }
   static constexpr int A_BYTES = TM * TK * 2;
   static constexpr int B_BYTES = TK * TN * 2;
   static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void ws_gemm_kernel(GemmParams p) {
     for (int q = 0; q < T::A_SHARE; ++q) {
       const int j = dw + DMA_WAVES * q;
       const int xx = 64 * j + lane, r = xx / T::CA, pos = xx % T::CA;
-      const int c = pos ^ (r % T::CA);
+      const int c = pos ^ T::a_swz(r);
       a_col[q] = 8 * c;
       a_off[q] = (m0 + r) * p.K + 8 * c;
     }
@@ -338,13 +343,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void ws_gemm_kernel(GemmParams p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hh = lane >> 5;
   // A^T operand: row m = wm*TM/2 + 32*mb + l32 of the A tile, chunk 2*s + hh
-  // of k-step s, stored at chunk ^ (row % CA). Offsets are slot-relative.
+  // of k-step s, stored at chunk ^ a_swz(row). Offsets are slot-relative.
   uint32_t a_off[KS][MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int r = wm * (TM / 2) + 32 * mb + l32;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) a_off[s][mb] = r * TK * 2 + 16 * ((2 * s + hh) ^ (r % T::CA));
+    for (int s = 0; s < KS; ++s) a_off[s][mb] = r * TK * 2 + 16 * ((2 * s + hh) ^ T::a_swz(r));
   }
   // B^T operand by ds_read_b64_tr_b16: in 16-lane group g, lane i reads 4
   // columns (col .. col+3) of k-row 8*(g/2) + i/4 (+ 16 s + 4 q), and
@@ -444,7 +449,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void ws_gemm_kernel(GemmParams p) {
     for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(af[LAST][mb]));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(bf[LAST][nb]));
-    asm volatile("ds_write_b32 %0, %1" ::"v"(released_lds), "v"((uint32_t)(i + 1)) : "memory");
+    // one lane writes: 64 lanes on one address would serialise on its bank
+    if (lane == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(released_lds), "v"((uint32_t)(i + 1)) : "memory");
     if (trace && wave == 0 && lane == 0) trace[i * TRACE_FIELDS + 3] = wall_clock64();
     const bool more = i + 1 < S;
     if (more) {

@@ -264,6 +264,89 @@ def test_fp8_k_and_v_tiles():
                 assert np.array_equal(got[lane], want), (b, rho, lane)
 
 
+# ---------------------------------------------------------------------------
+# Warp-specialised GEMM (row-major A [M][K] and B [K][N] tiles, fp16)
+# ---------------------------------------------------------------------------
+
+def gemm_a_swz(CA, r):
+    """A tile: chunk c of row r sits at chunk c ^ a_swz(r)."""
+    return (r >> 1) & 7 if CA == 8 else r & 15
+
+
+def gemm_b_swz(CB, kr):
+    return (4 if CB == 16 else 2) * (kr & 3)
+
+
+@pytest.mark.parametrize("TM,TN,TK", [(tm, tn, tk) for tm in (64, 128, 256) for tn in (64, 128)
+                                      for tk in (64, 128)])
+def test_gemm_tiles(TM, TN, TK):
+    """DMA fill of the A and B tiles (all DMA waves' loads together), then
+    the MATH waves' operands of C^T = B^T A^T: the A^T operand of wave
+    (wm, wn), row block mb, k-step s is row wm TM/2 + 32 mb + l32 and
+    k = 16 s + 8 hh .. +7 (one 16-byte read); the B^T operand of column
+    block nb is column wn TN/2 + 32 nb + l32 and the same k (two transposing
+    reads, 4 k each)."""
+    CA, CB = TK // 8, TN // 8
+    a_t = -np.ones(TM * TK, dtype=np.int64)  # LDS element -> m * TK + k
+    for j in range(TM * TK * 2 // 1024):
+        for lane in range(64):
+            xx = 64 * j + lane
+            r, pos = xx // CA, xx % CA
+            c = pos ^ gemm_a_swz(CA, r)
+            assert a_t[8 * xx] == -1
+            a_t[8 * xx:8 * xx + 8] = r * TK + 8 * c + np.arange(8)
+    assert sorted(a_t) == list(range(TM * TK))
+    b_t = -np.ones(TK * TN, dtype=np.int64)  # LDS element -> k * TN + n
+    for j in range(TK * TN * 2 // 1024):
+        for lane in range(64):
+            xx = 64 * j + lane
+            kr, pos = xx // CB, xx % CB
+            c = pos ^ gemm_b_swz(CB, kr)
+            assert b_t[8 * xx] == -1
+            b_t[8 * xx:8 * xx + 8] = kr * TN + 8 * c + np.arange(8)
+    assert sorted(b_t) == list(range(TK * TN))
+    for wm in range(2):
+        for mb in range(TM // 64):
+            for s in range(TK // 16):
+                addrs = []
+                for lane in range(64):
+                    l32, hh = lane % 32, lane // 32
+                    r = wm * (TM // 2) + 32 * mb + l32
+                    off = r * TK * 2 + 16 * ((2 * s + hh) ^ gemm_a_swz(CA, r))
+                    want = r * TK + 16 * s + 8 * hh + np.arange(8)
+                    assert np.array_equal(a_t[off // 2:off // 2 + 8], want)
+                    addrs.append(off)
+                assert conflict_free(addrs, 16), (wm, mb, s)
+    for wn in range(2):
+        for nb in range(TN // 64):
+            for s in range(TK // 16):
+                lo, hi = [], []
+                for lane in range(64):
+                    g, i = lane >> 4, lane & 15
+                    kr = 8 * (g >> 1) + (i >> 2)
+                    col = wn * (TN // 2) + 32 * nb + 16 * (g & 1) + 4 * (i & 3)
+                    c = (col >> 3) ^ gemm_b_swz(CB, kr)
+                    base = kr * TN * 2 + 16 * c + 2 * (col & 7) + 16 * s * TN * 2
+                    lo.append(base)
+                    hi.append(base + 4 * TN * 2)
+                assert conflict_free(lo, 8) and conflict_free(hi, 8), (wn, nb, s)
+                got = np.concatenate([tr_b16(b_t, lo), tr_b16(b_t, hi)], axis=1)
+                for lane in range(64):
+                    l32, hh = lane % 32, lane // 32
+                    n = wn * (TN // 2) + 32 * nb + l32
+                    want = (16 * s + 8 * hh + np.arange(8)) * TN + n
+                    assert np.array_equal(got[lane], want), (wn, nb, s, lane)
+
+
+def test_gemm_a_swizzle_by_row_alone_conflicts():
+    """With 128-byte A rows (T_K = 64), a swizzle that repeats every 8 rows
+    sends rows r and r + 8 of one 16-lane pass to the same banks: the
+    counters showed 4 conflict cycles per A read before the swizzle went to
+    row / 2."""
+    addrs = [(l % 32) * 128 + 16 * (0 ^ ((l % 32) % 8)) for l in range(64)]
+    assert not conflict_free(addrs, 16)
+
+
 def test_conflict_model_detects_conflicts():
     """Control: a plain row-major read of one column by 16 lanes conflicts."""
     assert not conflict_free([256 * l for l in range(64)], 16)

@@ -93,9 +93,21 @@ def test_chooser_picks_the_smallest_prediction(M, N, K):
                                    p.t_init) for c in ws_gemm.configs()}
     best = min(times.values())
     assert times[pick] <= best * (1 + 1e-9)
-    # of equal predictions for the picked tile, the deepest ring
+    # of equal predictions for the picked tile, the deepest ring that the
+    # stages can fill (or the shallowest, if none is that shallow)
     same = [c for c in times if c[:3] == pick[:3] and times[c] <= best * (1 + 1e-9)]
-    assert pick[3] == max(c[3] for c in same)
+    stages = -(-K // pick[2])
+    fill = [c[3] for c in same if c[3] <= stages]
+    assert pick[3] == (max(fill) if fill else min(c[3] for c in same))
+
+
+def test_chooser_ring_never_deeper_than_the_stages():
+    """K = 256 on T_K = 128 is two stages: rings 3 and 4 predict what ring 2
+    does, and the pick stays at two slots or fewer."""
+    p = make_params()
+    for M, N in ((256, 1024), (64, 64), (1024, 1024)):
+        tm, tn, tk, ring = ws_gemm.choose(M, N, 256, p)
+        assert ring <= -(-256 // tk)
 
 
 def test_config_list():
