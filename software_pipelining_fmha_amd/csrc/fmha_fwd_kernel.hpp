@@ -86,12 +86,22 @@ struct Tile {
   static constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
   static constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS
   static constexpr int SLOTS = 4;               // ring depth for K and for V
-  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
+  static constexpr int RING_BYTES = SLOTS * TILE_BYTES;
+  // O is staged from the start of the V ring, rows padded by 16 bytes
+  static constexpr int O_STRIDE = D * 2 + 16;
+  static constexpr int O_STAGE_BYTES = WAVES * QW * O_STRIDE;
+  static constexpr int LDS_BYTES = RING_BYTES + O_STAGE_BYTES;
+  // The next tile's Q goes to the K ring, once per wave: KSTEPS loads of
+  // 1 KB, load s holding every lane's k-step-s operand in lane order.
+  static_assert(WAVES * KSTEPS * 1024 == RING_BYTES, "one Q tile fills the K ring");
+  // VMEM instructions of the epilogue, per wave: O rows and lse
+  static constexpr int EPI_STORES = QW * D * 2 / 1024 + 1;
   // one tile = TILE_BYTES / 1024 wave-wide 16-byte-per-lane LDS-DMA loads
   static constexpr int LOADS_PER_TILE = TILE_BYTES / 1024;
   static constexpr int LOADS_PER_WAVE = LOADS_PER_TILE / WAVES;  // per tile
   static_assert(LOADS_PER_TILE % WAVES == 0 && LOADS_PER_WAVE >= 1, "tile loads split over waves");
   static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
+  static_assert(O_STAGE_BYTES >= RING_BYTES, "the V ring lies inside the O staging");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -155,16 +165,61 @@ __device__ __forceinline__ int k_chunk_off(int p, int c) {
   return (p * CPR + (c ^ k_swz<D>(p))) * 16;
 }
 
+// Staged Q rows -> registers: k-step s of lane l sits at base + 1024 s + 16 l.
+// One asm block issues every read and waits for them, so no output register
+// is taken as written before its data has landed.
+template <int KSTEPS>
+__device__ __forceinline__ void read_staged_q(uint32_t base, half8 (&qf)[KSTEPS]);
+template <>
+__device__ __forceinline__ void read_staged_q<8>(uint32_t base, half8 (&qf)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3]), "=&v"(qf[4]), "=&v"(qf[5]),
+        "=&v"(qf[6]), "=&v"(qf[7])
+      : "v"(base)
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_staged_q<4>(uint32_t base, half8 (&qf)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(qf[0]), "=&v"(qf[1]), "=&v"(qf[2]), "=&v"(qf[3])
+      : "v"(base)
+      : "memory");
+}
+
+// Tile t. Non-causal: t_next is the tile this workgroup runs next (-1:
+// none); once the last T stage is done, its Q rows go to the K ring by
+// LDS-DMA, and with q_staged the next call takes its Q from there instead of
+// from HBM, where every workgroup of the chip would request its Q at the
+// same moment (equal tiles turn over together). Causal tiles differ in
+// length and turn over at different times; staging measured slower there,
+// so the causal kernel loads Q at the tile's start.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw) {
+// `wave` is the caller's (uniform) wave index. In the non-causal kernel the
+// lane index is formed anew in every tile by an asm mbcnt the compiler
+// cannot hoist: otherwise it hoists every lane-derived constant out of the
+// tile loop, spills them (that kernel holds both passes and runs at 256
+// VGPRs), and each reload, a vector-memory load, waits for the previous
+// tile's stores. The causal kernel has the registers to keep them.
+__device__ __forceinline__ void fwd_tile(const Params& p, int t, int t_next, bool q_staged,
+                                         int wave, char* smem_raw) {
   using T = Tile<D>;
   typedef __attribute__((address_space(3))) char lds_char;
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int lane;
+  if constexpr (CAUSAL)
+    lane = threadIdx.x & 63;
+  else
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int group = wave >> 2;  // waves w and w + 4 share a SIMD
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -190,9 +245,27 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   const int wave_q_lo = q0 + wave * T::QW;
   const int qrow = wave_q_lo + l32;
   half8 qf[T::KSTEPS];
+  const uint32_t q_stage = (uint32_t)(uintptr_t)k_ring + wave * T::KSTEPS * 1024;
+  constexpr bool STAGE_Q = !CAUSAL;
+  if (STAGE_Q && q_staged) {
+    // The previous tile staged this wave's rows, and its epilogue's
+    // EPI_STORES stores are the only vector-memory operations since: once
+    // those older loads have landed in every wave, the rows are read, and a
+    // barrier keeps the K ring from being refilled before every wave has.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::EPI_STORES) : "memory");
+    // the lane offset is formed here, in asm the compiler cannot merge with
+    // `lane`: a register live from the tile's start may be spilled, and its
+    // reload (a vector-memory load) would wait for the epilogue's stores
+    uint32_t lane16;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 4, %0"
+                 : "=v"(lane16));
+    read_staged_q<T::KSTEPS>(q_stage + lane16, qf);
+    asm volatile("s_barrier" ::: "memory");
+  } else {
 #pragma unroll
-  for (int s = 0; s < T::KSTEPS; ++s)
-    qf[s] = __builtin_bit_cast(half8, load16(rq, (qrow * D + 16 * s + 8 * hh) * 2));
+    for (int s = 0; s < T::KSTEPS; ++s)
+      qf[s] = __builtin_bit_cast(half8, load16(rq, (qrow * D + 16 * s + 8 * hh) * 2));
+  }
   // The C stage needs a positive multiplier (its row max is taken on the raw
   // scores, and masked scores are -inf). So the sign of scale rides on Q,
   // where multiplying by -1 or 0 is exact: (-q).k * |scale| = q.k * scale,
@@ -521,8 +594,13 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // 2t+3. Each wait is vmcnt(0): a vector interval issues K_{j+3} and
   // V_{j+2}, and nothing more before the end of the next matrix-core
   // interval. The next DMA into a K slot (tile t+4) is issued in global 2t+3
-  // or later, into a V slot in global 2t+5 or later. Loads past the sequence
-  // end return zeros into slots that are never read.
+  // or later, into a V slot in global 2t+5 or later. The prologue's five
+  // DMAs go out whatever the sequence length (past its end they land zeros
+  // in slots that are never read); later intervals issue only tiles below
+  // n_kv. The last interval, j = n_kv, comes after every wave's last T stage
+  // (group 1's in global 2 n_kv - 1, its lead-operand reads in global 2 n_kv),
+  // so the K ring is idle from then on: there each wave sends its share of
+  // the next tile's Q there.
   auto sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
   auto mfma_sync = [&]() __attribute__((always_inline)) {
     // this wave's K_{j+2} and V_{j+1} DMAs landed
@@ -532,9 +610,26 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     // this wave's operand reads for the next interval are done
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
+  // With Q staging no DMA goes past the key sequence: a zero fill still in
+  // flight into the K ring could land on the staged Q.
   auto produce = [&](int j) __attribute__((always_inline)) {
-    fetch_k(j + 3);
-    fetch_v(j + 2);
+    if (!STAGE_Q || j + 3 < n_kv) fetch_k(j + 3);
+    if (!STAGE_Q || j + 2 < n_kv) fetch_v(j + 2);
+  };
+  // The next tile's Q rows, this wave's share, into the K ring (k-step s of
+  // lane l at q_stage + 1024 s + 16 l). Without a next tile the loads read
+  // past the buffer (zeros), so that every tile issues the same count.
+  auto fetch_q_next = [&]() __attribute__((always_inline)) {
+    const int tn = t_next < 0 ? t : t_next;
+    const int bh_n = tn / p.n_qt;
+    int qt_n = tn - bh_n * p.n_qt;
+    if (CAUSAL) qt_n = p.n_qt - 1 - qt_n;
+    const __amdgpu_buffer_rsrc_t rq_n = make_rsrc(p.q + (size_t)bh_n * (size_t)N * D, head_bytes);
+    const int off = t_next < 0 ? 0x7ffffff0 - 32 * T::KSTEPS
+                               : ((qt_n * T::BM + wave * T::QW + l32) * D + 8 * hh) * 2;
+#pragma unroll
+    for (int s = 0; s < T::KSTEPS; ++s)
+      load16_to_lds(rq_n, off + 32 * s, k_ring + wave * T::KSTEPS * 1024 + 1024 * s);
   };
 
   // Steady-state iteration j (1 <= j < n_wave) with K slot U = j % 4 known
@@ -613,13 +708,14 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
       if (j == n_wave && j >= 1) last_pv(j);
       mfma_sync();
       produce(j);
+      if (STAGE_Q && j == n_kv) fetch_q_next();
       vector_sync();
     }
     if (group == 0) sync();
-    // Every wave's trailing DMAs (tiles past the end, zeros) have landed once
-    // all waves pass this barrier: the epilogue and the rerun check reuse the
-    // rings, across the waves' shares, right after it.
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // Every wave's DMAs but the staged Q loads have landed once all waves
+    // pass this barrier: the epilogue and the rerun check reuse the V ring
+    // (and without staging the K ring too), across the waves' shares.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(STAGE_Q ? T::KSTEPS : 0) : "memory");
   };
   // The causal kernel holds the exact pass only: with the fast pass and its
   // rerun compiled in as well, it ran 10% slower on a causal workload with
@@ -643,6 +739,9 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
     any = __builtin_amdgcn_readfirstlane(any);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (any) {
+      // the next tile's Q is still landing in the K ring, which the rerun
+      // refills (it stages that Q again at its end)
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int b = 0; b < T::DBLK; ++b) oacc[b] = floatx16{};
       lacc = floatx4{};
@@ -655,14 +754,14 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   // lanes q and q + 32 hold query q; the row sum sits in lane q (lane q + 32 has 0)
   const float l_tot = sum_halves(lacc[0]);
   const float inv = 1.f / l_tot;
-  // O goes through LDS (the rings are idle now) so that the global stores
-  // are whole rows: each wave writes its 32 rows of fp16 O into a region of
-  // its own, rows padded by 16 bytes (a 32-lane write of one d column then
-  // hits each bank at most twice, and the 16-byte row reads stay aligned and
+  // O goes through LDS (the V ring and the padding after it are idle now;
+  // the K ring holds the next tile's Q) so that the global stores are whole
+  // rows: each wave writes its 32 rows of fp16 O into a region of its own,
+  // rows padded by 16 bytes (a 32-lane write of one d column then hits each
+  // bank at most twice, and the 16-byte row reads stay aligned and
   // conflict-free), and stores 16 bytes per lane, D / 8 lanes per row.
-  constexpr int O_STRIDE = D * 2 + 16;
-  static_assert(T::WAVES * T::QW * O_STRIDE <= T::LDS_BYTES, "O staging fits the rings");
-  lds_char* const ob = k_ring + wave * T::QW * O_STRIDE;
+  constexpr int O_STRIDE = T::O_STRIDE;
+  lds_char* const ob = v_ring + wave * T::QW * O_STRIDE;
 #pragma unroll
   for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
@@ -675,14 +774,20 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, char* smem_raw)
   constexpr int LANES_PER_ROW = D / 8;
   constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
   const int srow = lane / LANES_PER_ROW, scol = 8 * (lane % LANES_PER_ROW);
+  // Raw-buffer stores, rows at or past N out of range (dropped): every wave
+  // issues exactly EPI_STORES of them, which the next tile's wait counts on.
+  static_assert(T::QW / ROWS_PER_STORE + 1 == T::EPI_STORES, "epilogue store count");
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4u);
 #pragma unroll
   for (int r0 = 0; r0 < T::QW; r0 += ROWS_PER_STORE) {
     const int row = r0 + srow;
     const half8 x = *(const __attribute__((address_space(3))) half8*)(ob + row * O_STRIDE + 2 * scol);
-    if (wave_q_lo + row < N) *reinterpret_cast<half8*>(p.o + head + (size_t)(wave_q_lo + row) * D + scol) = x;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, x), ro,
+                                           ((wave_q_lo + row) * D + scol) * 2, 0, 0);
   }
-  if (qrow < N && hh == 0)
-    p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse_v), rl, hh == 0 ? qrow * 4 : 0x7ffffff0, 0, 0);
   // the next tile's DMAs may refill the rings only once every wave has read
   // its staged rows back
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -702,12 +807,19 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p)
   // draws a light one next. Tile ids map to (b, h, query tile) so that one
   // XCD's tiles are consecutive ids (one head's query tiles share its L2).
   const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
-  for (int r = 0; r * (int)gridDim.x < G; ++r) {
+  auto tile_of = [&](int r) {
     const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
-    if (tile >= G) break;
-    const int t = x * per + min(x, rem) + (tile >> 3);
-    fwd_tile<D, CAUSAL>(p, t, smem_raw);
+    return tile < G ? x * per + min(x, rem) + (tile >> 3) : -1;
+  };
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int r = 0;; ++r) {
+    const int t = tile_of(r);
+    if (t < 0) break;
+    // a non-causal tile stages the next one's Q (see fwd_tile)
+    fwd_tile<D, CAUSAL>(p, t, tile_of(r + 1), r > 0, wave, smem_raw);
   }
+  // a non-causal workgroup's last tile staged Q loads past the buffer
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace fmha

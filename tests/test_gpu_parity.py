@@ -141,6 +141,34 @@ def test_late_scores_far_above_first_key_tile(d, causal, device):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_overflow_rerun_with_many_tiles(d, device):
+    """More query tiles than compute units, so each workgroup runs several
+    and stages the next tile's Q while finishing the current one. Rows
+    500..539 of every head in batch 0 overflow the fast pass (a late key
+    2^28 above the first key tile), so their tiles rerun exactly; the rerun
+    refills the K ring that held the staged Q, and the next tile must still
+    see its own Q. The overflow rows and both edges of every tile match the
+    oracle."""
+    torch = torch_mod()
+    B, H, N = 3, 31, 1000
+    bm = fmha.fmha_query_tile(d)
+    tiles = B * H * (-(-N // bm))
+    assert tiles > torch.cuda.get_device_properties(0).multi_processor_count
+    print("overflow rerun, many tiles d=%d tiles=%d" % (d, tiles), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=1900 + d)
+    q[0, :, 500:540, 7] = 16
+    k[0, :, 64:, 7] = 16
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, False, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rows = list(map(tuple, tile_edge_rows(B, H, N, bm, seed=1900 + d)))
+    rows += [(0, h, i) for h in (0, 17, 30) for i in (500, 519, 539)]
+    rows = np.array(rows, dtype=np.int64)
+    o_ref, lse_ref = oracle.fmha_rows(q, k, v, rows, causal=False, scale=scale)
+    check_rows(o, lse, rows, o_ref, lse_ref, "overflow rerun, many tiles")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_late_scores_just_inside_fp16_weights(d, device):
     """Keys past the first tile score 2^13 to 2^15 above the first tile's
     max: the weights stay finite but reach thousands, with no rescale."""
@@ -265,10 +293,13 @@ def test_non_default_stream(device):
     assert np.array_equal(ref[0].view(np.uint16), got[0].view(np.uint16))
 
 
-def test_guard_bands_untouched(device):
-    """Writes stay inside o and lse: sentinels around both are unchanged."""
+@pytest.mark.parametrize("B,H,N,causal", [(2, 2, 333, True), (3, 31, 1000, False)])
+def test_guard_bands_untouched(B, H, N, causal, device):
+    """Writes stay inside o and lse: sentinels around both are unchanged.
+    The second case runs several tiles per workgroup with a ragged last
+    query tile (its rows past N are dropped stores and zero Q loads)."""
     torch = torch_mod()
-    B, H, N, d = 2, 2, 333, 128
+    d = 128
     q, k, v = inputs.draw_qkv(B, H, N, d, seed=15)
     tq, tk, tv = to_dev(q, k, v)
     pad = 4096
@@ -276,7 +307,7 @@ def test_guard_bands_untouched(device):
     lb = torch.full((B * H * N + 2 * pad,), -777.0, dtype=torch.float32, device="cuda:0")
     o = ob[pad:pad + B * H * N * d].view(B, H, N, d)
     lse = lb[pad:pad + B * H * N].view(B, H, N)
-    fmha.forward(tq, tk, tv, causal=True, scale=0.088388, out=o, lse=lse)
+    fmha.forward(tq, tk, tv, causal=causal, scale=0.088388, out=o, lse=lse)
     torch.cuda.synchronize()
     obc, lbc = ob.cpu().numpy(), lb.cpu().numpy()
     assert (obc[:pad] == np.float16(12345.0)).all() and (obc[-pad:] == np.float16(12345.0)).all()
