@@ -72,9 +72,23 @@ struct Fp8Tile {
   static constexpr int RUNS = BN / 16;            // runs of 8 keys per V^T operand half
   static constexpr int TILE_BYTES = BN * D;       // one K or V tile
   static constexpr int SLOTS = 4;                 // ring depth for K and for V
-  static constexpr int LDS_BYTES = 2 * SLOTS * TILE_BYTES;
+  static constexpr int RING_BYTES = SLOTS * TILE_BYTES;
+  // O (fp16) is staged from the start of the V ring, rows padded by 16 bytes
+  static constexpr int O_STRIDE = D * 2 + 16;
+  static constexpr int O_STAGE_BYTES = WAVES * QW * O_STRIDE;
+  static constexpr int LDS_BYTES = RING_BYTES + O_STAGE_BYTES;
+  // K loads past the key sequence land in this 1 KB (inside the O staging,
+  // past the V ring), not in the K ring that may hold the next tile's Q
+  static constexpr int JUNK_OFFSET = 2 * RING_BYTES;
+  static_assert(JUNK_OFFSET + 1024 <= LDS_BYTES, "junk line inside the LDS block");
   static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / WAVES;  // per tile
   static_assert(LOADS_PER_WAVE == 1, "one 16-byte DMA per lane per tile");
+  // The next tile's Q: 4 KB per wave in the K ring, four 1 KB loads, load i
+  // holding bytes 64 (i / 2) + 32 hh + 16 (i % 2) .. +15 of each lane's row
+  static constexpr int Q_LOADS = QW * D / 1024;
+  static_assert(WAVES * Q_LOADS * 1024 == RING_BYTES && Q_LOADS == 2 * KSTEPS, "one Q tile fills the K ring");
+  // VMEM instructions of the epilogue, per wave: O rows and lse
+  static constexpr int EPI_STORES = QW * D * 2 / 1024 + 1;
 };
 
 // 16-byte chunk swizzles (8 chunks per 128-byte row). K: 16 consecutive rows
@@ -94,8 +108,13 @@ __device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
 // reference), so on sharp softmax rows most tiles pay for both passes. The
 // causal kernel holds the exact pass only: with both passes compiled in, its
 // exact pass ran 5% slower on sharp inputs.
+// Non-causal tiles stage the next tile's Q rows in the idle K ring after
+// their last T stage (t_next: -1 for none), and with q_staged a tile takes
+// its Q from there, as the FP16 kernel does; the causal kernel loads Q at the
+// tile's start.
 template <bool CAUSAL>
-__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* smem_raw) {
+__device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, int t_next, bool q_staged,
+                                             char* smem_raw) {
   using T = Fp8Tile;
   constexpr int D = T::D;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -104,9 +123,15 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
   lds_char* const k_ring = (lds_char*)smem_raw;
   lds_char* const v_ring = k_ring + T::SLOTS * T::TILE_BYTES;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Non-causal: the lane index is formed per tile by an asm mbcnt the
+  // compiler cannot hoist out of the tile loop (it would spill the hoisted
+  // lane constants, as in the FP16 kernel).
+  int lane;
+  if constexpr (CAUSAL)
+    lane = threadIdx.x & 63;
+  else
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int group = wave >> 2;  // waves w and w + 4 share a SIMD
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -127,11 +152,32 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
   const int wave_q_lo = q0 + wave * T::QW;
   const int qrow = wave_q_lo + l32;
   intx8 qf[T::KSTEPS];
+  constexpr bool STAGE_Q = !CAUSAL;
+  static_assert(T::KSTEPS == 2, "four staged 16-byte reads");
+  if (STAGE_Q && q_staged) {
+    // the previous tile's epilogue (EPI_STORES stores) is all that was
+    // issued since the staged loads; a barrier keeps the K ring from being
+    // refilled before every wave has read its rows
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::EPI_STORES) : "memory");
+    const uint32_t qs = (uint32_t)(uintptr_t)k_ring + wave * T::Q_LOADS * 1024 + 16 * lane;
+    intx4 a0, a1, a2, a3;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+        : "v"(qs)
+        : "memory");
+    asm volatile("s_barrier" ::: "memory");
+    qf[0] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    qf[1] = __builtin_shufflevector(a2, a3, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
 #pragma unroll
-  for (int s = 0; s < T::KSTEPS; ++s) {
-    const intx4 a = load16(rq, qrow * D + 64 * s + 32 * hh);
-    const intx4 b = load16(rq, qrow * D + 64 * s + 32 * hh + 16);
-    qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int s = 0; s < T::KSTEPS; ++s) {
+      const intx4 a = load16(rq, qrow * D + 64 * s + 32 * hh);
+      const intx4 b = load16(rq, qrow * D + 64 * s + 32 * hh + 16);
+      qf[s] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   }
   // The C stage needs a positive multiplier, so the sign of scale rides on Q.
   if (p.q_and != 0xffffffffu || p.q_xor != 0u) {
@@ -173,9 +219,24 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     k_src = ((r & ~31) | key_of_row(r & 31)) * D + 16 * (pos ^ fp8_k_swz(r));
     v_src = r * D + 16 * (pos ^ fp8_v_swz(r));
   }
+  // Every interval issues one K and one V load per wave (the waits count
+  // them). With Q staging, K loads past the sequence go to the junk line.
   auto fetch_k = [&](int j) __attribute__((always_inline)) {
     load16_to_lds(rk, j * T::TILE_BYTES + k_src,
-                  k_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * 1024);
+                  (STAGE_Q && j >= n_kv) ? (lds_char*)smem_raw + T::JUNK_OFFSET
+                                         : k_ring + (j % T::SLOTS) * T::TILE_BYTES + wave * 1024);
+  };
+  // The next tile's Q rows, this wave's share, into the K ring; without a
+  // next tile the loads read past the buffer (zeros), so the count is fixed.
+  auto fetch_q_next = [&]() __attribute__((always_inline)) {
+    const int tn = t_next < 0 ? t : t_next;
+    const int bh_n = tn / p.n_qt;
+    const int qt_n = tn - bh_n * p.n_qt;
+    const __amdgpu_buffer_rsrc_t rq_n = make_rsrc(p.q + (size_t)bh_n * (size_t)N * D, head_bytes);
+    const int off = t_next < 0 ? 0x7ffffff0 - 128 : (qt_n * T::BM + wave * T::QW + l32) * D + 32 * hh;
+#pragma unroll
+    for (int i = 0; i < T::Q_LOADS; ++i)
+      load16_to_lds(rq_n, off + 64 * (i >> 1) + 16 * (i & 1), k_ring + wave * T::Q_LOADS * 1024 + 1024 * i);
   };
   auto fetch_v = [&](int j) __attribute__((always_inline)) {
     load16_to_lds(rv, j * T::TILE_BYTES + v_src,
@@ -494,18 +555,23 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
       if (j == n_wave && j >= 1) pv(j - 1, std::integral_constant<bool, !decltype(exact_tag)::value>{});
       mfma_sync();
       produce_issue(j);
+      // every wave is past its last T stage (group 1's reads end one
+      // interval earlier), so the K ring is idle from here on
+      if (STAGE_Q && j == n_kv) fetch_q_next();
       vector_sync();
     }
     if (group == 0) sync();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // every DMA but the staged Q loads has landed in every wave: the V ring
+    // (and the O staging beyond it) may be reused
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(STAGE_Q ? T::Q_LOADS : 0) : "memory");
   };
   // true in every wave if `mine` holds in some lane of some wave. The flags
-  // sit in the K ring, which trailing DMAs of other waves may still be
-  // writing until every wave has passed its vmcnt(0).
+  // sit in the V ring (idle after the pipeline's last wait; the K ring may
+  // be receiving the next tile's Q).
   auto any_wave = [&](bool mine) __attribute__((always_inline)) {
     const bool bad = __builtin_amdgcn_ballot_w64(mine) != 0;
     sync();
-    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)k_ring;
+    __attribute__((address_space(3))) int* flags = (__attribute__((address_space(3))) int*)v_ring;
     if (lane == 0) flags[wave] = bad ? 1 : 0;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     int any = 0;
@@ -519,6 +585,9 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
     run_pipeline(std::integral_constant<bool, CAUSAL>{});
     // A weight that overflowed E4M3 is NaN, and so is its row sum.
     if (any_wave(!(sum_halves(lacc[0]) < INFINITY))) {
+      // the staged Q for the next tile is landing in the K ring, which the
+      // rerun refills (and stages again at its end)
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int b = 0; b < T::DBLK; ++b) oacc[b] = floatx16{};
       lacc = floatx4{};
@@ -531,21 +600,41 @@ __device__ __forceinline__ void fwd_fp8_tile(const Fp8Params& p, int t, char* sm
 
   // ---- epilogue: O = descale_v O_acc / l, lse = (m + log2 l) ln 2 ---------------
   // register i of block b holds d = 32 b + 8 (i / 4) + 4 hh + i % 4
+  // O goes through LDS so that the global stores are whole rows (as in the
+  // FP16 kernel): each wave stages its 32 rows from the start of the V ring,
+  // rows padded by 16 bytes, and stores 16 bytes per lane, 16 lanes per row,
+  // by raw-buffer stores (rows past N out of range): exactly EPI_STORES per
+  // wave, which the next tile's wait for its staged Q counts on.
   const float l_tot = sum_halves(lacc[0]);
   const float f = p.descale_v / l_tot;
-  if (qrow < N) {
-    _Float16* orow = p.o + head + (size_t)qrow * D;
+  constexpr int O_STRIDE = T::O_STRIDE;
+  lds_char* const ob = v_ring + wave * T::QW * O_STRIDE;
 #pragma unroll
-    for (int b = 0; b < T::DBLK; ++b)
+  for (int b = 0; b < T::DBLK; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        half4 w = {(_Float16)(oacc[b][4 * g + 0] * f), (_Float16)(oacc[b][4 * g + 1] * f),
-                   (_Float16)(oacc[b][4 * g + 2] * f), (_Float16)(oacc[b][4 * g + 3] * f)};
-        *reinterpret_cast<half4*>(orow + 32 * b + 8 * g + 4 * hh) = w;
-      }
-    if (hh == 0)
-      p.lse[(size_t)bh * N + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    for (int g = 0; g < 4; ++g) {
+      half4 w = {(_Float16)(oacc[b][4 * g + 0] * f), (_Float16)(oacc[b][4 * g + 1] * f),
+                 (_Float16)(oacc[b][4 * g + 2] * f), (_Float16)(oacc[b][4 * g + 3] * f)};
+      *(__attribute__((address_space(3))) half4*)(ob + l32 * O_STRIDE + (32 * b + 8 * g + 4 * hh) * 2) = w;
+    }
+  constexpr int LANES_PER_ROW = D / 8;
+  constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
+  static_assert(T::QW / ROWS_PER_STORE + 1 == T::EPI_STORES, "epilogue store count");
+  const int srow = lane / LANES_PER_ROW, scol = 8 * (lane % LANES_PER_ROW);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + head, head_bytes * 2u);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4u);
+#pragma unroll
+  for (int r0 = 0; r0 < T::QW; r0 += ROWS_PER_STORE) {
+    const int row = r0 + srow;
+    const half8 x = *(const __attribute__((address_space(3))) half8*)(ob + row * O_STRIDE + 2 * scol);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, x), ro,
+                                           ((wave_q_lo + row) * D + scol) * 2, 0, 0);
   }
+  const float lse_v = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(lse_v), rl, hh == 0 ? qrow * 4 : 0x7ffffff0, 0, 0);
+  // the next tile's DMAs may refill the V ring only once every wave has read
+  // its staged rows back
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Persistent, with the FP16 kernel's tile schedule: one workgroup per CU (a
@@ -556,11 +645,17 @@ __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Pa
   const int G = p.total_wg;
   const int per = G >> 3, rem = G & 7;
   const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
-  for (int r = 0; r * (int)gridDim.x < G; ++r) {
+  auto tile_of = [&](int r) {
     const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
-    if (tile >= G) break;
-    fwd_fp8_tile<CAUSAL>(p, x * per + min(x, rem) + (tile >> 3), smem_raw);
+    return tile < G ? x * per + min(x, rem) + (tile >> 3) : -1;
+  };
+  for (int r = 0;; ++r) {
+    const int t = tile_of(r);
+    if (t < 0) break;
+    fwd_fp8_tile<CAUSAL>(p, t, tile_of(r + 1), r > 0, smem_raw);
   }
+  // a non-causal workgroup's last tile staged Q loads past the buffer
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace fmha
