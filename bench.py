@@ -580,7 +580,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 100 for --pass gemm)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default 5; 50 for --pass gemm)")
+                    help="untimed steps first (default 10; 20 for --dtype fp8, 50 for --pass gemm, "
+                         "5 for --pass bwd)")
     ap.add_argument("--workload", default=inputs.WORKLOADS[inputs.HEADLINE].name,
                     choices=[w.name for w in inputs.WORKLOADS] + [w.name for w in inputs.FP8_WORKLOADS]
                     + [w.name for w in inputs.GEMM_WORKLOADS])
@@ -601,12 +602,21 @@ def main(argv=None) -> int:
                     help="instead of attention, run a plain device copy of this many MiB "
                          "per step (calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args(argv)
-    # A GEMM launch takes about 1 ms: the clocks need some 50 of them to
-    # settle, and the default 5 + 20 would time the ramp.
+    # The clocks ramp over the first launches: about 50 ms for the GEMM and
+    # the FP8 forward (which run below the power limit), a few launches for
+    # the FP16 forward. The default warm-up covers the ramp, so that the
+    # timed steps see the steady state.
     if args.steps is None:
         args.steps = 100 if args.which == "gemm" else 20
     if args.warmup is None:
-        args.warmup = 50 if args.which == "gemm" else 5
+        if args.which == "gemm":
+            args.warmup = 50
+        elif args.which == "bwd":
+            args.warmup = 5
+        elif args.dtype == "fp8":
+            args.warmup = 20
+        else:
+            args.warmup = 10
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the attention forward pass here is a "
