@@ -604,36 +604,6 @@ struct DqTile {
   static_assert(BT == BwdTile<D>::BT, "the dQ grid tiles 128 queries like the other kernels");
 };
 
-// The four transposed A operands (16-key k-steps 0..3) of one 32-row d
-// block of K^T: eight ds_read_b64_tr_b16 in one asm block that also waits
-// for them. As a builtin the compiler cannot tell that these reads miss the
-// slot an LDS-DMA is filling, and waits for every DMA in flight before each.
-// a0 and a1 address the two 4-row halves of k-step 0; k-step ks adds
-// 16 rows (KS_BYTES).
-template <int KS_BYTES>
-__device__ __forceinline__ void tr_block4(uint32_t a0, uint32_t a1, half8 (&out)[4]) {
-  shortx4 r[8];
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
-      "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
-      "ds_read_b64_tr_b16 %6, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-        "=&v"(r[7])
-      : "v"(a0), "v"(a1), "n"(KS_BYTES), "n"(2 * KS_BYTES), "n"(3 * KS_BYTES)
-      : "memory");
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const half4 lo = __builtin_bit_cast(half4, r[2 * k]), hi = __builtin_bit_cast(half4, r[2 * k + 1]);
-    out[k] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdParams p) {
   using T = DqTile<D>;
@@ -724,7 +694,9 @@ __global__ __launch_bounds__(DqTile<D>::THREADS, 2) void fmha_bwd_dq_kernel(BwdP
   // i); dQ MFMA i: k-step i / DBLK over the step's keys, d block i % DBLK.
   // Consecutive MFMAs never share an accumulator. Each operand is read
   // AHEAD MFMAs before its use and waited for alone (LDS reads complete in
-  // order); the reads are inline asm for the reason given at tr_block4.
+  // order). The reads are inline asm: as builtins the compiler cannot tell
+  // that they miss the slot an LDS-DMA is filling, and it waits for every
+  // DMA in flight before each.
   constexpr int NSD = 4 * T::KSTEPS, NDQ = 4 * T::DBLK, AHEAD = OPERAND_AHEAD;
   static_assert(T::KB == 2 && NSD >= AHEAD && NDQ >= AHEAD, "interval shapes");
   auto sd_operand = [&](auto slot_tag, int i) __attribute__((always_inline)) {
