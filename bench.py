@@ -695,12 +695,16 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         o_host, lse_host = o.cpu().numpy(), lse.cpu().numpy()
-        cb, parity = cpu_baseline(q, k, v, w, scale, o_host, lse_host, args.cpu_seconds)
-        cb.pop("seconds")
+        try:
+            cb, parity = cpu_baseline(q, k, v, w, scale, o_host, lse_host, args.cpu_seconds)
+            cb.pop("seconds")
+        except Exception as e:  # the GPU measurement stands; the line says why the CPU leg is missing
+            cb = {"value": None, "unit": "TFLOPS", "kind": "oracle", "error": "%s: %s" % (type(e).__name__, e)}
+            parity = {"pass": None, "error": "the CPU oracle did not run"}
         result["cpu_baseline"] = cb
         result["parity"] = parity
     print(json.dumps(result), flush=True)
-    if "parity" in result and not result["parity"]["pass"]:
+    if "parity" in result and result["parity"]["pass"] is False:
         return 1
     return 0
 
