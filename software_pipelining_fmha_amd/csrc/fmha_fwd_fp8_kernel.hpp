@@ -651,12 +651,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(Fp8Tile::THREADS, 1) void fmha_fwd_fp8_kernel(Fp8Params p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[Fp8Tile::LDS_BYTES];
   const int G = p.total_wg;
-  const int per = G >> 3, rem = G & 7;
-  const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
-  auto tile_of = [&](int r) {
-    const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
-    return tile < G ? x * per + min(x, rem) + (tile >> 3) : -1;
-  };
+  auto tile_of = [&](int r) { return persistent_tile(r, G); };
   for (int r = 0;; ++r) {
     const int t = tile_of(r);
     if (t < 0) break;

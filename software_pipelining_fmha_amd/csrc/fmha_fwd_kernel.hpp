@@ -793,24 +793,32 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, int t_next, boo
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Persistent schedule (Tawa, sections IV-B and V-E: launch as many
+// workgroups as the chip holds and let them iterate over tiles), shared by
+// the FP16 and FP8 forward kernels. Workgroup b runs on
+// XCD b % 8; the grid is either every tile (one each) or a multiple of 8 no
+// larger than the CU count. Pass r hands out slots r * grid .. r * grid +
+// grid - 1, walking the workgroups of each XCD in reverse on odd passes, so
+// that a workgroup that drew a heavy causal tile draws a light one next.
+// Slots map to tile ids so that one XCD's tiles are consecutive ids (one
+// head's tiles share its L2). Returns -1 once this workgroup has no tile in
+// pass r. With one workgroup per tile there is only pass 0: the reversed
+// walk is a permutation of a pass only when the grid is a multiple of 8.
+__device__ __forceinline__ int persistent_tile(int r, int G) {
+  const int grid = gridDim.x;
+  if (r * grid >= G) return -1;
+  const int g8 = grid >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
+  const int slot = r * grid + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
+  if (slot >= G) return -1;
+  const int per = G >> 3, rem = G & 7;
+  return x * per + min(x, rem) + (slot >> 3);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(Tile<D>::THREADS, 1) void fmha_fwd_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[Tile<D>::LDS_BYTES];
   const int G = p.total_wg;
-  const int per = G >> 3, rem = G & 7;
-  // Persistent schedule (Tawa, sections IV-B and V-E: launch as many
-  // workgroups as the chip holds and let them iterate over tiles). Workgroup
-  // b runs on XCD b % 8; the grid is either every tile (one each) or a
-  // multiple of 8 no larger than the CU count. Pass r hands out tiles
-  // r * grid .. r * grid + grid - 1, walking the workgroups of each XCD in
-  // reverse on odd passes, so that a workgroup that drew a heavy causal tile
-  // draws a light one next. Tile ids map to (b, h, query tile) so that one
-  // XCD's tiles are consecutive ids (one head's query tiles share its L2).
-  const int g8 = gridDim.x >> 3, b8 = blockIdx.x >> 3, x = blockIdx.x & 7;
-  auto tile_of = [&](int r) {
-    const int tile = r * gridDim.x + 8 * ((r & 1) ? g8 - 1 - b8 : b8) + x;
-    return tile < G ? x * per + min(x, rem) + (tile >> 3) : -1;
-  };
+  auto tile_of = [&](int r) { return persistent_tile(r, G); };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int r = 0;; ++r) {
     const int t = tile_of(r);
