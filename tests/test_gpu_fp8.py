@@ -90,6 +90,24 @@ def test_fp8_workload_parity(idx, device):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_fp8_one_workgroup_per_tile_grid_not_a_multiple_of_8(causal, device):
+    """12 query tiles: one workgroup per tile and a single pass, the grid on
+    which the reversed walk of an odd pass falls below the tile count. Every
+    output is written and every row matches the oracle."""
+    B, H, N, d = 1, 3, 1024, 128
+    tiles = B * H * (-(-N // 256))
+    assert tiles < 256 and tiles % 8
+    print("fp8 one workgroup per tile causal=%d tiles=%d" % (causal, tiles), flush=True)
+    b, sc = inputs.draw_qkv_fp8(B, H, N, d, seed=6500 + causal)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(b, sc, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rows = np.array([(0, h, i) for h in range(H) for i in range(N)], dtype=np.int64)
+    ref = oracle.fmha_fp8_rows(*b, sc, rows, causal=causal, scale=scale, rss=True)
+    check(o, lse, rows, ref, "fp8 one workgroup per tile")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp8_persistent_passes_cover_every_tile(causal, device):
     """More query tiles than compute units, not a multiple of 8: several
     passes per workgroup with a partial last one. Every output is written

@@ -239,6 +239,26 @@ def test_persistent_passes_cover_every_tile(d, causal, device):
     check_rows(o, lse, rows, o_ref, lse_ref, "persistent cover")
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 1, 600, False), (1, 3, 1024, True), (3, 5, 1000, False)])
+def test_one_workgroup_per_tile_grid_not_a_multiple_of_8(B, H, N, causal, device):
+    """Fewer query tiles than compute units and not a multiple of 8 (3, 12
+    and 60 tiles): one workgroup per tile and a single pass, the grid on
+    which the reversed walk of an odd pass falls below the tile count.
+    Every output is written and every row matches the oracle."""
+    d = 128
+    bm = fmha.fmha_query_tile(d)
+    tiles = B * H * (-(-N // bm))
+    assert tiles < 256 and tiles % 8
+    print("one workgroup per tile: tiles=%d causal=%d" % (tiles, causal), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=1900 + tiles)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    o_ref, lse_ref = oracle.fmha_all(q, k, v, causal=causal, scale=scale)
+    assert np.abs(o.astype(np.float64) - o_ref).max() <= TOL_O
+    assert np.abs(lse.astype(np.float64) - lse_ref).max() <= TOL_LSE
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_first_row_is_first_value_row(d, device):
     q, k, v = inputs.draw_qkv(2, 2, 257, d, seed=12)
