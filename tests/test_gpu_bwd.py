@@ -171,11 +171,12 @@ def test_full_size_key_and_value_gradient_sums(causal, device):
     assert (sk <= bk).all() and (sv <= bv).all()
 
 
-def test_deterministic_bitwise(device):
+@pytest.mark.parametrize("causal", [True, False])
+def test_deterministic_bitwise(causal, device):
     q, k, v = inputs.draw_qkv(2, 4, 1000, 128, seed=61)
     do = inputs.draw_dout(2, 4, 1000, 128, seed=62)
-    a = run_bwd(q, k, v, do, True, np.float32(0.088388))
-    b = run_bwd(q, k, v, do, True, np.float32(0.088388))
+    a = run_bwd(q, k, v, do, causal, np.float32(0.088388))
+    b = run_bwd(q, k, v, do, causal, np.float32(0.088388))
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
 
