@@ -109,17 +109,6 @@ __global__ __launch_bounds__(256) void fmha_bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Shared pieces of the two streaming kernels
 // ---------------------------------------------------------------------------
-// Transposed A operand (8 rows of one d column per lane) from two
-// ds_read_b64_tr_b16 reads.
-__device__ __forceinline__ half8 tr_pair(const __attribute__((address_space(3))) char* base, int off0,
-                                         int off1) {
-  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + off0));
-  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + off1));
-  const half4 a = __builtin_bit_cast(half4, lo), b = __builtin_bit_cast(half4, hi);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Per-lane byte offsets into a streamed [BS][D] tile.
 // nat[s]: A operand of row key_of_row(l32) (MFMA row l32), d = 16 s + 8 hh .. +7.
 // tr[b][rd]: source of ds_read_b64_tr_b16 for the transposed A operand of

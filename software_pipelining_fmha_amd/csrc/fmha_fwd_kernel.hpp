@@ -122,13 +122,9 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, int byte
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, byte_off, 0, 0, 0);
 }
 
-// Value of x combined with the partner lane (lane ^ 32) via v_permlane32_swap.
-// After the swap the two results hold {x[l], x[l^32]} in some order, so they
-// are combined with a symmetric operation.
-__device__ __forceinline__ float max_halves(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// x plus the partner lane's x (lane ^ 32), via v_permlane32_swap. After the
+// swap the two results hold {x[l], x[l^32]} in some order; the sum is
+// symmetric, so every lane gets the same value.
 __device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);

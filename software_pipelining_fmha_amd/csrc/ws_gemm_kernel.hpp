@@ -179,14 +179,6 @@ __device__ __forceinline__ bool wait_full_geq(const lds_char* cnt, uint32_t targ
   return false;
 }
 
-// ds_read_b64_tr_b16: in each 16-lane group, lane i supplies the address of
-// 4 consecutive halves of row i/4 of a 4 x 16 block and receives column i
-// of its 4 rows. (A device function of its own: the builtin exists only for
-// gfx950, and the host pass must still see a valid kernel template.)
-__device__ __forceinline__ shortx4 read_tr16(const lds_char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)p);
-}
-
 __device__ __forceinline__ void store_counter(lds_char* cnt, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(cnt)), "v"(v) : "memory");
 }
