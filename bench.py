@@ -576,11 +576,37 @@ def copy_calibration(mib: int, steps: int) -> int:
     return 0
 
 
+# Default length of the timed region. A couple of seconds of back-to-back
+# launches is long enough for an outside utilisation sampler to see and for
+# the per-launch spread to average out; a 60-s run of the FP16 headline held
+# the same rate as its first seconds.
+TIMED_SECONDS = 2.0
+MAX_DEFAULT_STEPS = 4000
+# TFLOPS each pass reaches at its headline shape (counted FLOPs), used only to
+# size the default step count.
+USUAL_TFLOPS = {"fwd": 1200.0, "fp8": 2300.0, "bwd": 800.0}
+
+
+def _default_steps(args) -> int:
+    if args.which == "gemm":
+        return 100
+    fp8 = args.dtype == "fp8"
+    pool = inputs.FP8_WORKLOADS if fp8 else inputs.WORKLOADS
+    name = args.workload if (not fp8 or args.workload.startswith("fp8_")) else "fp8_" + args.workload
+    w = next((x for x in pool if x.name == name), None)
+    if w is None or args.which not in ("fwd", "bwd"):
+        return 20
+    flops = w.flops * (2.5 if args.which == "bwd" else 1.0)
+    rate = USUAL_TFLOPS["fp8" if fp8 else args.which] * 1e12
+    return int(min(MAX_DEFAULT_STEPS, max(20, round(TIMED_SECONDS * rate / flops))))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; 100 for --pass gemm)")
+                    help="timed steps (default: about %.0f s of work at the pass's usual rate, "
+                         "20 to %d steps; 100 for --pass gemm)" % (TIMED_SECONDS, MAX_DEFAULT_STEPS))
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default 10; 20 for --dtype fp8, 50 for --pass gemm, "
                          "5 for --pass bwd)")
@@ -609,7 +635,7 @@ def main(argv=None) -> int:
     # the FP16 forward. The default warm-up covers the ramp, so that the
     # timed steps see the steady state.
     if args.steps is None:
-        args.steps = 100 if args.which == "gemm" else 20
+        args.steps = _default_steps(args)
     if args.warmup is None:
         if args.which == "gemm":
             args.warmup = 50
