@@ -601,7 +601,9 @@ def _default_steps(args) -> int:
     return int(min(MAX_DEFAULT_STEPS, max(20, round(TIMED_SECONDS * rate / flops))))
 
 
-def main(argv=None) -> int:
+def parse_args(argv=None) -> argparse.Namespace:
+    """The command line, with the per-pass default step and warm-up counts
+    filled in."""
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
@@ -645,7 +647,11 @@ def main(argv=None) -> int:
             args.warmup = 20
         else:
             args.warmup = 10
+    return args
 
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the attention forward pass here is a "
               "single-GPU kernel with no cross-GPU path (asked for --gpus %d)" % args.gpus,
