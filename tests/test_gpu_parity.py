@@ -371,6 +371,29 @@ def test_zero_scale_is_the_mean_of_visible_values(causal, device):
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("causal,k_gain", [(False, 1.0), (True, 3.0)])
+def test_head_dim_64_at_full_size(causal, k_gain, device):
+    """The d = 64 kernels at B4 H32 N4096 (512 query tiles, two persistent
+    passes): 256 seeded rows plus, for causal, the tile-edge rows of 4 heads
+    at the d = 64 kernel's own tile sizes. The causal case draws K scaled by 3
+    (sharp rows, the exact pass's lazy rescale) as the d = 128 causal
+    workload does."""
+    B, H, N, d = 4, 32, 4096, 64
+    print("d=64 full size causal=%d k_gain=%g" % (causal, k_gain), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=6400 + causal, k_gain=k_gain)
+    scale = np.float32(1 / math.sqrt(d))
+    o, lse = run(q, k, v, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), "unwritten output"
+    rows = inputs.sample_rows(B, H, N, 256, seed=64 + causal)
+    if causal:
+        bm, bn = fmha.fmha_query_tile(d), fmha.fmha_key_tile(d)
+        extra = inputs.boundary_rows(B, H, N, 4, seed=65, tiles=(32, bn, 128, bm))
+        assert {bm - 1, bm, bn - 1, bn} <= set(extra[:, 2].tolist())
+        rows = np.unique(np.concatenate([rows, extra]), axis=0)
+    o_ref, lse_ref = oracle.fmha_rows(q, k, v, rows, causal=causal, scale=scale)
+    check_rows(o, lse, rows, o_ref, lse_ref, "d=64 full size")
+
+
 def test_empty_problem_launches_nothing(device):
     torch = torch_mod()
     q = torch.empty((0, 2, 16, 64), dtype=torch.float16, device="cuda:0")
