@@ -149,6 +149,31 @@ def test_workload_sampled_rows(idx, device):
     check("dv", dv[b, h, j], ref[2], ref[5], w.name)
 
 
+@pytest.mark.parametrize("causal,k_gain", [(False, 1.0), (True, 3.0)])
+def test_head_dim_64_at_full_size(causal, k_gain, device):
+    """The d = 64 backward kernels at B4 H32 N4096 (the d = 128 checks' launch
+    configuration, at the other head dim): dq on 256 seeded rows, dk and dv
+    on 32 key rows of each of 2 seeded heads, including keys 0 and N-1."""
+    B, H, N, d = 4, 32, 4096, 64
+    print("bwd d=64 full size causal=%d k_gain=%g" % (causal, k_gain), flush=True)
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed=6500 + causal, k_gain=k_gain)
+    do = inputs.draw_dout(B, H, N, d, seed=6600 + causal)
+    scale = np.float32(1 / math.sqrt(d))
+    dq, dk, dv = run_bwd(q, k, v, do, causal, scale)
+    qrows = inputs.sample_rows(B, H, N, 256, seed=66 + causal)
+    rng = np.random.default_rng(67 + causal)
+    heads = rng.choice(B * H, size=2, replace=False)
+    keys = [np.sort(np.concatenate([[0, N - 1], rng.choice(np.arange(1, N - 1), size=30, replace=False)]))
+            for _ in heads]
+    krows = np.array([(hh // H, hh % H, j) for hh, ks in zip(heads, keys) for j in ks])
+    ref = oracle.fmha_bwd_rows(q, k, v, do, qrows, krows, causal=causal, scale=scale, rss=True)
+    b, h, i = qrows.T
+    check("dq", dq[b, h, i], ref[0], ref[3], "d=64 full size", ref[6])
+    b, h, j = krows.T
+    check("dk", dk[b, h, j], ref[1], ref[4], "d=64 full size", ref[7])
+    check("dv", dv[b, h, j], ref[2], ref[5], "d=64 full size")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_full_size_key_and_value_gradient_sums(causal, device):
     """Every row of a full-size problem (B4 H32 N8192 d128): per head
