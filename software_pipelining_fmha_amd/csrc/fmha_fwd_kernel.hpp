@@ -716,9 +716,11 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, int t_next, boo
   // The causal kernel holds the exact pass only: with the fast pass and its
   // rerun compiled in as well, it ran 10% slower on a causal workload with
   // sharp softmax rows (K scaled by 3) and 2% faster on one with plain N(0,1)
-  // keys. The fast pass itself is the cheaper one there too; what costs is a
-  // rerun of a heavy causal tile (up to N / 64 key tiles), which finishes
-  // after every other workgroup has drained and so lengthens the launch.
+  // keys. The fast pass itself is the cheaper one there too; what costs is
+  // the reruns' own work. They fall on the heavy causal tiles (up to N / 64
+  // key tiles), which have the most chances of a late score far above their
+  // first key tile's max; handing tiles out dynamically, so that a rerun only
+  // means fewer later tiles, still left the fast pass 2% behind there.
   if constexpr (CAUSAL) {
     run_pipeline(std::true_type{});
   } else {
