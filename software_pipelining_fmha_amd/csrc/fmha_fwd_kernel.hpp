@@ -52,7 +52,11 @@ typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 
-// Reference-max slack (base 2) before O and l are rescaled.
+// Reference-max slack (base 2) before O and l are rescaled; every weight
+// then stays at or below 2^slack. The FP16 kernel takes 15: fp16 holds up
+// to 65504, and on sharp rows a wider slack means fewer rescales. The FP8
+// kernel takes 8, since E4M3 holds no more than 448.
+constexpr float RESCALE_LOG2_F16 = 15.0f;
 constexpr float RESCALE_LOG2 = 8.0f;
 // MFMA slots by which an LDS operand read precedes its MFMA.
 constexpr int OPERAND_AHEAD = 4;
@@ -473,7 +477,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, int t_next, boo
   // C stage for key tile j. The weights are first formed against the current
   // reference max; the row max, computed alongside, only decides whether the
   // reference must move. It moves only when some row's max grows by more than
-  // 2^RESCALE_LOG2, so p <= 2^RESCALE_LOG2 always. O and l share the
+  // 2^RESCALE_LOG2_F16, so p <= 2^RESCALE_LOG2_F16 always. O and l share the
   // reference, so O / l is unchanged when it stays. When it moves, O and l
   // are rescaled (they hold every earlier tile here: U_{j-1} and its row sum
   // ran in the matrix-core interval before C_j) and the weights are formed
@@ -492,7 +496,7 @@ __device__ __forceinline__ void fwd_tile(const Params& p, int t, int t_next, boo
 #pragma unroll
     for (int st = 0; st < T::PSTEPS; ++st) asm volatile("" : "+v"(pf[st]));
     const float m_tile = tile_max();
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2) != 0) {
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + RESCALE_LOG2_F16) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
